@@ -1,0 +1,382 @@
+"""Pins for the oracle's element and scale codecs, Philox and the Hadamard
+transform, each against something other than the oracle itself: enumeration,
+brute force with exact rationals, a library routine (torch float8_e4m3fn,
+scipy's Hadamard matrix, rocRAND's open-source Philox engine), published
+known-answer vectors, closed forms and statistical bounds.
+
+Method source: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1
+elements, E4M3 block scales, 16x16 random Hadamard transforms with random
+signs, stochastic rounding for gradients.
+"""
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- E2M1 ----
+def test_e2m1_enumeration():
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    assert vals[:8] == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert vals[8:] == [-v for v in vals[:8]]
+    assert math.copysign(1.0, vals[8]) == -1.0  # code 0x8 is -0
+
+
+def _rtn_rational(y: float) -> int:
+    """Nearest grid point by exact rational distance, ties to even code, saturating."""
+    sign = 8 if math.copysign(1.0, y) < 0 else 0
+    a = abs(Fraction(y))
+    if a >= 6:
+        return sign | 7
+    d = [abs(a - g) for g in GRID]
+    best = min(d)
+    cands = [i for i in range(8) if d[i] == best]
+    if len(cands) == 2:
+        cands = [i for i in cands if i % 2 == 0]
+    return sign | cands[0]
+
+
+def _interesting_f32():
+    pts = set()
+    for g in GRID:
+        pts.add(float(g))
+    for i in range(7):
+        pts.add(float((GRID[i] + GRID[i + 1]) / 2))
+    pts |= {6.5, 7.0, 100.0, 1e30, 3.4e38, 1e-45, 1e-40, 1e-30, 0.1, 0.3}
+    out = []
+    for p in pts:
+        f = np.float32(p)
+        out += [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))]
+    out = np.array(out, dtype=np.float32)
+    out = out[np.isfinite(out)]
+    return np.concatenate([out, -out])
+
+
+def test_e2m1_rtn_against_exact_rationals():
+    rng = np.random.default_rng(11)
+    rand_bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    rand = rand_bits.view(np.float32)
+    rand = rand[np.isfinite(rand)]
+    small = rng.uniform(-7, 7, size=20000).astype(np.float32)
+    ys = np.concatenate([_interesting_f32(), rand, small])
+    got = oracle.e2m1_encode_rtn(ys)
+    want = np.array([_rtn_rational(float(y)) for y in ys], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def _rtn_thresholds(y: np.ndarray) -> np.ndarray:
+    """The hand-derived threshold form of nearest-even E2M1 rounding."""
+    a = np.abs(y.astype(np.float64))
+    mag = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5)
+           + (a > 5.0))
+    sign = (np.signbit(y).astype(np.uint8) << 3)
+    return (mag | sign).astype(np.uint8)
+
+
+def test_e2m1_rtn_exhaustive_band_against_thresholds():
+    # every fp32 bit pattern with magnitude in [2^-3, 8), both signs
+    lo = np.float32(0.125).view(np.uint32)
+    hi = np.float32(8.0).view(np.uint32)
+    step = 1 << 22
+    for start in range(int(lo), int(hi), step):
+        cnt = min(step, int(hi) - start)
+        got = oracle.e2m1_encode_rtn_bits(start, cnt)
+        ys = np.arange(start, start + cnt, dtype=np.uint32).view(np.float32)
+        assert np.array_equal(got, _rtn_thresholds(ys))
+        got_neg = oracle.e2m1_encode_rtn_bits(start | 0x80000000, cnt)
+        assert np.array_equal(got_neg, _rtn_thresholds(-ys))
+
+
+def test_e2m1_rtn_golden_thresholds():
+    # tests/golden/e2m1_rtn_cases.txt: value -> code, derived by hand from the
+    # E2M1 grid {0,.5,1,1.5,2,3,4,6} with ties to the even mantissa bit.
+    path = os.path.join(GOLDEN, "e2m1_rtn_cases.txt")
+    ys, codes = [], []
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        v, c = line.split()
+        ys.append(float(v))
+        codes.append(int(c, 16))
+    assert np.array_equal(oracle.e2m1_encode_rtn(np.array(ys, dtype=np.float32)), np.array(codes, dtype=np.uint8))
+
+
+# ---------------------------------------------------------------- SR ------
+def _neighbours(a: Fraction):
+    a = min(a, Fraction(6))
+    i = max(k for k in range(8) if GRID[k] <= a)
+    if GRID[i] == a:
+        return i, i, Fraction(0)
+    return i, i + 1, (a - GRID[i]) / (GRID[i + 1] - GRID[i])
+
+
+@pytest.mark.parametrize("y", [0.1, 0.3, 0.7, 0.74999994, 1.1, 1.3, 1.9, 2.2, 2.9, 3.3, 3.9, 4.4, 5.9, 5.0, 2.5,
+                               1e-6, 1e-39, 0.25, 0.5000001, 6.0000005, 9.0])
+def test_sr_enumerates_exact_round_up_count(y):
+    u = np.arange(65536, dtype=np.uint16)
+    for s in (1.0, -1.0):
+        yy = np.float32(s * y)
+        got = oracle.e2m1_encode_sr(np.full(65536, yy, dtype=np.float32), u)
+        lo, hi, frac = _neighbours(abs(Fraction(float(yy))))
+        sign = 8 if s < 0 else 0
+        assert set(np.unique(got).tolist()) <= {sign | lo, sign | hi}
+        n_up = int(np.count_nonzero(got == (sign | hi))) if hi != lo else 0
+        assert n_up == math.ceil(frac * 65536)
+        # round-ups are exactly the smallest u16 values
+        if n_up:
+            assert np.all(got[:n_up] == (sign | hi)) and np.all(got[n_up:] == (sign | lo))
+
+
+def test_sr_grid_values_are_fixed_points():
+    u = np.arange(0, 65536, 7, dtype=np.uint16)
+    for c in range(16):
+        y = np.float32(oracle.e2m1_value(c))
+        got = oracle.e2m1_encode_sr(np.full(u.shape, y, dtype=np.float32), u)
+        assert np.all(got == c)
+
+
+def test_sr_unbiased_over_philox_draws():
+    n = 100_000
+    blocks = np.arange(n, dtype=np.uint64) // 16
+    js = (np.arange(n) % 16).astype(np.int32)
+    u = oracle.sr_uniform_array(1234, blocks, js)
+    for lo_i in range(7):
+        lo, hi = float(GRID[lo_i]), float(GRID[lo_i + 1])
+        step = hi - lo
+        for p in (0.1, 0.25, 0.5, 0.9):
+            y = np.float32(lo + p * step)
+            codes = oracle.e2m1_encode_sr(np.full(n, y, dtype=np.float32), u)
+            vals = np.array([oracle.e2m1_value(c) for c in range(16)])[codes]
+            mean = vals.mean()
+            pp = (float(y) - lo) / step
+            bound = 5 * step * math.sqrt(pp * (1 - pp) / n) + step * 2.0 ** -16
+            assert abs(mean - float(y)) <= bound, (lo_i, p, mean, float(y), bound)
+
+
+def test_sr_uniforms_are_uniform():
+    # 16-bit uniforms from distinct counters: chi-square over 256 bins of the top byte
+    n = 1 << 18
+    blocks = np.arange(n, dtype=np.uint64) // 16
+    js = (np.arange(n) % 16).astype(np.int32)
+    u = oracle.sr_uniform_array(99, blocks, js)
+    h = np.bincount(u >> 8, minlength=256)
+    exp = n / 256
+    chi2 = float(((h - exp) ** 2 / exp).sum())
+    assert chi2 < 400  # 255 dof: mean 255, sd ~22.6
+
+
+# ---------------------------------------------------------------- E4M3 ----
+def test_e4m3_enumeration():
+    v = [oracle.e4m3_value(c) for c in range(256)]
+    assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x3F] == 1.875 and v[0x7E] == 448.0
+    assert math.isnan(v[0x7F]) and math.isnan(v[0xFF])
+    pos = np.array(v[:0x7F])
+    assert np.all(np.diff(pos) > 0)  # strictly increasing over the finite codes
+    assert all(v[0x80 + c] == -v[c] for c in range(0x7F))
+
+
+def test_e4m3_decode_matches_torch():
+    torch = pytest.importorskip("torch")
+    codes = torch.arange(256, dtype=torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    ov = np.array([oracle.e4m3_value(c) for c in range(256)], dtype=np.float32)
+    fin = np.isfinite(ov)
+    assert np.array_equal(np.isnan(tv), ~fin)
+    assert np.array_equal(tv[fin], ov[fin])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    # dense fp32 coverage of [2^-12, 512) (every 5th bit pattern), plus every
+    # E4M3 value and midpoint with +/-3 ulp neighbours
+    lo = int(np.float32(2.0 ** -12).view(np.uint32))
+    hi = int(np.float32(512.0).view(np.uint32))
+    dense = np.arange(lo, hi, 5, dtype=np.uint32).view(np.float32)
+    vals = np.array([oracle.e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids, [448.0, 464.0, 480.0, 500.0, 1e6, 0.0]]).astype(np.float32)
+    nb = [pts]
+    for k in range(1, 4):
+        up, dn = pts.copy(), pts.copy()
+        for _ in range(k):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(0))
+        nb += [up, dn]
+    xs = np.concatenate([dense] + nb).astype(np.float32)
+    xs = xs[xs >= 0]
+    got = oracle.e4m3_encode(xs)
+    want = torch.from_numpy(xs).clamp(0, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- Philox --
+def _philox_py(key, ctr):
+    """Second, independent Philox4x32-10 written with Python integers."""
+    M0, M1, W0, W1 = 0xD2511F53, 0xCD9E8D57, 0x9E3779B9, 0xBB67AE85
+    mask = 0xFFFFFFFF
+    k = list(key)
+    c = list(ctr)
+    for r in range(10):
+        p0 = M0 * c[0]
+        p1 = M1 * c[2]
+        c = [((p1 >> 32) ^ c[1] ^ k[0]) & mask, p1 & mask, ((p0 >> 32) ^ c[3] ^ k[1]) & mask, p0 & mask]
+        k = [(k[0] + W0) & mask, (k[1] + W1) & mask]
+    return c
+
+
+def test_philox_known_answers():
+    # tests/golden/philox4x32_10_kat.txt: known-answer vectors published with
+    # Random123 (Salmon et al., SC'11) for philox4x32 with 10 rounds.
+    for line in open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        w = [int(t, 16) for t in line.split()]
+        ctr, key, want = w[0:4], w[4:6], w[6:10]
+        assert oracle.philox4x32_10(key, ctr)[0].tolist() == want
+        assert _philox_py(key, ctr) == want
+
+
+def test_philox_against_python_random_grid():
+    rng = np.random.default_rng(5)
+    keys = rng.integers(0, 2**32, size=(300, 2), dtype=np.uint64).astype(np.uint32)
+    ctrs = rng.integers(0, 2**32, size=(300, 4), dtype=np.uint64).astype(np.uint32)
+    got = oracle.philox4x32_10(keys, ctrs)
+    for i in range(300):
+        assert got[i].tolist() == _philox_py(keys[i].tolist(), ctrs[i].tolist())
+
+
+ROCRAND_PROBE = r"""
+#include <rocrand/rocrand_philox4x32_10.h>
+#include <cstdio>
+struct Exposed : rocrand_device::philox4x32_10_engine {
+  using rocrand_device::philox4x32_10_engine::ten_rounds;  // protected in the engine
+};
+int main() {
+  Exposed e;
+  unsigned k0, k1, c0, c1, c2, c3;
+  while (scanf("%x %x %x %x %x %x", &c0, &c1, &c2, &c3, &k0, &k1) == 6) {
+    uint4 r = e.ten_rounds(uint4{c0, c1, c2, c3}, uint2{k0, k1});
+    printf("%08x %08x %08x %08x\n", r.x, r.y, r.z, r.w);
+  }
+  return 0;
+}
+"""
+
+
+def test_philox_against_rocrand_engine():
+    """Library routine: rocRAND's open-source Philox4x32-10 engine (host build)."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"):
+        pytest.skip("rocRAND headers or hipcc not available")
+    rng = np.random.default_rng(6)
+    keys = rng.integers(0, 2**32, size=(200, 2), dtype=np.uint64).astype(np.uint32)
+    ctrs = rng.integers(0, 2**32, size=(200, 4), dtype=np.uint64).astype(np.uint32)
+    ctrs[:4] = [[0, 0, 0, 0], [0, 0, 1, 0], [1, 0, 0, 0], [0xFFFFFFFF] * 4]
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "p.cpp")
+        exe = os.path.join(d, "p")
+        open(src, "w").write(ROCRAND_PROBE)
+        r = subprocess.run([hipcc, "-x", "hip", "--offload-arch=gfx950", "-O1", "-o", exe, src],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            pytest.skip("could not build the rocRAND host probe: " + r.stderr[-300:])
+        inp = "\n".join("%x %x %x %x %x %x" % (*c, *k) for c, k in zip(ctrs.tolist(), keys.tolist()))
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout.split("\n")
+    got = oracle.philox4x32_10(keys, ctrs)
+    for i in range(200):
+        assert [int(t, 16) for t in out[i].split()] == got[i].tolist()
+
+
+def test_sr_uniform_counter_convention():
+    # parity unpinned convention, checked for internal consistency: element j of
+    # block b takes half (j & 1) of word (j & 7) >> 1 of Philox(seed, (2b + j>>3, 0, 0, 0))
+    seed = 0x1234_5678_9ABC
+    for b in (0, 1, 77, 2**33 + 5):
+        for j in range(16):
+            g = 2 * b + (j >> 3)
+            w = _philox_py([seed & 0xFFFFFFFF, seed >> 32], [g & 0xFFFFFFFF, g >> 32, 0, 0])
+            assert oracle.sr_uniform(seed, b, j) == (w[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFF
+
+
+# ---------------------------------------------------------------- RHT -----
+def _rht_matrix(mask):
+    return np.stack([oracle.rht16(np.eye(16)[j], mask) for j in range(16)], axis=1)  # column j = Q e_j
+
+
+def test_rht_is_scaled_sylvester_hadamard():
+    scipy_linalg = pytest.importorskip("scipy.linalg")
+    H = scipy_linalg.hadamard(16).astype(np.float64)
+    assert np.array_equal(H @ H.T, 16 * np.eye(16))
+    assert np.array_equal(_rht_matrix(0), H / 4)
+    mask = 0b1010_0110_0001_1101
+    D = np.diag([-1.0 if (mask >> j) & 1 else 1.0 for j in range(16)])
+    assert np.array_equal(_rht_matrix(mask), H @ D / 4)
+
+
+def test_rht_orthonormal_inverse_and_gram():
+    rng = np.random.default_rng(3)
+    mask = oracle.rht_sign_mask(1234)
+    Q = _rht_matrix(mask)
+    assert np.allclose(Q @ Q.T, np.eye(16), atol=0, rtol=0)
+    v = rng.standard_normal(16)
+    z = oracle.rht16(v, mask)
+    assert np.allclose(Q.T @ z, v, rtol=1e-15, atol=1e-15)
+    A = rng.standard_normal((16, 40))
+    B = rng.standard_normal((16, 30))
+    QA = np.stack([oracle.rht16(A[:, i], mask) for i in range(40)], axis=1)
+    QB = np.stack([oracle.rht16(B[:, i], mask) for i in range(30)], axis=1)
+    assert np.allclose(QA.T @ QB, A.T @ B, rtol=1e-12, atol=1e-12)
+
+
+def test_rht_exact_for_bf16_inputs():
+    # 16 bf16 values spanning a few binades: the binary64 transform is exact, so
+    # applying the inverse reproduces the input bit-for-bit
+    rng = np.random.default_rng(8)
+    from nvfp4_bit_quantization_amd.synthetic import bf16_bits_to_f32, f32_to_bf16_bits
+    for _ in range(50):
+        v = bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal(16).astype(np.float32))).astype(np.float64)
+        mask = int(rng.integers(0, 65536))
+        z = oracle.rht16(v, mask)
+        Q = _rht_matrix(mask)
+        assert np.array_equal(Q.T @ z, v)
+
+
+def test_rht_sign_mask_convention():
+    # parity unpinned convention: low 16 bits of word 0 of Philox(seed, (0,0,1,0))
+    for seed in (0, 1, 1234, 4321, 2**40 + 3):
+        w = _philox_py([seed & 0xFFFFFFFF, seed >> 32], [0, 0, 1, 0])
+        assert oracle.rht_sign_mask(seed) == w[0] & 0xFFFF
+
+
+# ---------------------------------------------------------------- bf16 ----
+def test_f64_to_bf16_matches_torch_for_f32_inputs():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    bits = rng.integers(0, 2**32, size=200000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    x = np.concatenate([x, rng.standard_normal(100000).astype(np.float32)])
+    got = oracle.f64_to_bf16_bits(x.astype(np.float64))
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_f64_to_bf16_single_rounding():
+    # 1 + 2^-8 + 2^-40 lies just above a bf16 midpoint; rounding through fp32
+    # first would land exactly on the midpoint and round to even (1.0)
+    assert oracle.f64_to_bf16_bits(np.array([1 + 2.0 ** -8 + 2.0 ** -40]))[0] == 0x3F81
+    assert oracle.f64_to_bf16_bits(np.array([1 + 2.0 ** -8]))[0] == 0x3F80
+    assert oracle.f64_to_bf16_bits(np.array([-(1 + 3 * 2.0 ** -8)]))[0] == 0xBF82
