@@ -1,0 +1,172 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: NVFP4 tensor quantisation and the
+ * NVFP4-operand GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * The method follows the NVFP4 pretraining news page (zubnet.ai,
+ * "nvidia-nvfp4-paper-4-bit-pretrain-hits-fp8-parity-12b-10t-tokens"),
+ * paragraph 2: E2M1 elements in blocks of 16, one E4M3 scale per block, an
+ * FP32 per-tensor scale over the whole tensor; 1D blocks for activations and
+ * gradients, 16x16 2D blocks for weights (so a weight and its transpose
+ * quantise identically), stochastic rounding for gradients only, and a 16x16
+ * random Hadamard transform (RHT) with random +/-1 signs on the inputs of the
+ * weight-gradient GEMM.  Paragraph 1 gives the GEMM's role (the 4-bit matrix
+ * products that replace FP8 ones).
+ *
+ * Arithmetic convention (all binary32, round-to-nearest-even, no FMA):
+ *   amax  = max |v| over the tensor (v = the RHT output when rht is set)
+ *   S     = 2688 / amax  (2688 = 448 * 6); S = 1 if amax == 0 or S is not finite
+ *   per block b: sb = (amax_b / 6) * S; s_b = E4M3(sb), nearest-even, saturating
+ *   at 448, subnormals kept; r_b = S / s_b (0 if s_b == 0)
+ *   per element: y = v * r_b, then E2M1 nearest-even (saturating at 6) or
+ *   stochastic rounding with a 16-bit Philox4x32-10 uniform
+ *   dequantised value = (e(code) * s_b) / S.
+ *
+ * Storage:
+ *   codes  : packed E2M1, [rows][cols/2] bytes, element 2i in the low nibble;
+ *            code bit 3 = sign, codes 0..7 = 0, .5, 1, 1.5, 2, 3, 4, 6
+ *   scales : E4M3 (OCP E4M3FN) bytes, 1D: [rows][cols/16]; 2D: [rows/16][cols/16]
+ *   "rows x cols" is the stored orientation; cols is the blocked (K) dimension.
+ *
+ * Conventions common to every entry point:
+ *   - every data pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates nothing, keeps no state and is reentrant;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and nothing synchronises the host; outputs are valid once the stream
+ *     reaches that point, and inputs must not change before then;
+ *   - arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is written and a negative status is returned;
+ *   - inputs must be finite (NaN/Inf give unspecified outputs).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define NVFP4_OK 0
+#define NVFP4_E_NULL (-1)        /* a required pointer is NULL */
+#define NVFP4_E_SHAPE (-2)       /* a size <= 0, not a multiple of 16, or inconsistent */
+#define NVFP4_E_LD (-3)          /* a leading dimension smaller than the row length */
+#define NVFP4_E_ALIGN (-4)       /* x, codes or y not 16-byte aligned, or ld not a multiple of 8 */
+#define NVFP4_E_UNSUPPORTED (-5) /* unknown enum, RHT with a 2D layout, bad n_outs, K mismatch */
+#define NVFP4_E_WORKSPACE (-6)   /* workspace NULL or smaller than nvfp4_workspace_bytes() */
+#define NVFP4_E_HIP (-7)         /* a HIP launch failed */
+
+/* layouts of one quantised output of an input x[rows][cols] */
+#define NVFP4_ROW_1D 0 /* 1D blocks of 16 along cols; stored [rows][cols] */
+#define NVFP4_COL_1D 1 /* 1D blocks of 16 along rows; stored transposed [cols][rows] */
+#define NVFP4_2D 2     /* 16x16 tiles; stored [rows][cols], scales [rows/16][cols/16] */
+#define NVFP4_2D_T 3   /* the NVFP4_2D results stored transposed [cols][rows], scales [cols/16][rows/16] */
+
+/* rounding */
+#define NVFP4_RTN 0 /* nearest, ties to even mantissa bit */
+#define NVFP4_SR 1  /* stochastic, Philox4x32-10 keyed by sr_seed */
+
+/* scale kinds of a quantised tensor */
+#define NVFP4_SCALE_1D16 0
+#define NVFP4_SCALE_2D16 1
+
+/* GEMM output dtypes */
+#define NVFP4_F32 0
+#define NVFP4_BF16 1
+
+/* A quantised tensor in its stored orientation (rows x cols, cols = K). */
+typedef struct {
+  uint8_t *codes;       /* [rows][cols/2] packed E2M1 */
+  uint8_t *scales;      /* E4M3: 1D [rows][cols/16]; 2D [rows/16][cols/16] */
+  float *global_scale;  /* 1 float: S = 2688 / amax */
+  float *amax;          /* 1 float: amax of what was quantised (after the RHT if any) */
+  int64_t rows;
+  int64_t cols;
+  int32_t scale_kind;   /* NVFP4_SCALE_1D16 or NVFP4_SCALE_2D16 */
+  int32_t rht;          /* 1 if the codes hold RHT-domain values (informational) */
+} nvfp4_tensor;
+
+/* One requested output of nvfp4_quantize.  `out` must describe buffers of the
+ * shape implied by `layout` (rows/cols in the stored orientation, scale_kind
+ * matching the layout). */
+typedef struct {
+  int32_t layout;     /* NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_2D, NVFP4_2D_T */
+  int32_t rounding;   /* NVFP4_RTN or NVFP4_SR */
+  int32_t rht;        /* 1: 16x16 RHT along the blocked dim; 1D layouts only */
+  int32_t reserved;   /* must be 0 */
+  uint64_t sr_seed;   /* Philox key of the stochastic rounding */
+  uint64_t rht_seed;  /* Philox key of the RHT sign vector */
+  nvfp4_tensor out;
+} nvfp4_quant_output;
+
+/*
+ * nvfp4_quantize -- quantise x (bf16, [rows][cols], row stride ld_x elements)
+ * into one or two outputs from a single pass over x.
+ *
+ * Defines: page paragraph 2 (format, 1D/2D block scaling, stochastic rounding
+ * on gradients, RHT on Wgrad inputs).
+ *   x          device, bf16, 16-byte aligned, ld_x >= cols, ld_x % 8 == 0
+ *   rows, cols multiples of 16
+ *   outs       host array of n_outs (1 or 2) output descriptors.  With two
+ *              outputs the pair must be {ROW_1D, COL_1D} (either order, any
+ *              rounding/RHT each) or {2D, 2D_T}; two outputs sharing RHT
+ *              settings share the amax.
+ *   workspace  device scratch of at least nvfp4_workspace_bytes() bytes
+ *              (per-workgroup partial maxima; no initialisation needed)
+ * Enqueues two kernels (amax pass, quantise pass) on `stream`.
+ * Writes codes, scales, *global_scale and *amax of every output.
+ * RHT signs: d_j = -1 iff bit (j mod 16) of nvfp4_rht_sign_mask(rht_seed),
+ * j the index along the blocked dimension.
+ * Returns NVFP4_OK or a negative status (nothing enqueued).
+ */
+int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
+                   int n_outs, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace nvfp4_quantize needs (a small constant). */
+size_t nvfp4_workspace_bytes(void);
+
+/*
+ * nvfp4_dequantize -- y[r][c] = (e(code) * s_b) / S for the stored
+ * orientation of q, as fp32 with row stride ld_y elements.
+ * Defines: page paragraph 2 (block scale times element, over the per-tensor
+ * scale).  q->codes, q->scales, q->global_scale and y are device pointers;
+ * y 16-byte aligned, ld_y >= q->cols, ld_y % 4 == 0.
+ */
+int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream);
+
+/*
+ * nvfp4_gemm -- C[m][n] = (sum_k A^[m][k] * B^[n][k]) / (S_A * S_B), where
+ * A^ = e(code) * s_b is the exact operand value.
+ * Defines: page paragraph 1 (the 4-bit GEMMs) with the scales of paragraph 2.
+ *   a : M x K quantised tensor (a->rows = M, a->cols = K)
+ *   b : N x K quantised tensor (b->rows = N, b->cols = K); a->cols == b->cols
+ *   c : device, [M][N] with row stride ldc elements, fp32 or bf16 (RNE)
+ * Operands are expanded exactly to fp16 in LDS and multiplied on MFMA with
+ * fp32 accumulation; the per-tensor scales are applied in the epilogue.
+ */
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *stream);
+
+/* Host: the 16-bit RHT sign mask for a seed (bit j set => d_j = -1):
+ * the low 16 bits of word 0 of Philox4x32-10(key = seed, counter = (0,0,1,0)). */
+uint16_t nvfp4_rht_sign_mask(uint64_t rht_seed);
+
+/* Host: a static description of a status code. */
+const char *nvfp4_status_string(int status);
+
+/*
+ * Codec self-test hooks (for the exhaustive hardware checks in the tests):
+ * run the device's element/scale encoders exactly as the quantise kernels use
+ * them.  which = 0: E2M1 round-to-nearest of in_f32[i] -> out_u8[i];
+ * which = 1: E2M1 stochastic rounding of in_f32[i] with uniform in_u16[i];
+ * which = 2: E4M3 of the non-negative in_f32[i].  in_u16 is read for which = 1
+ * only.  n >= 0; all pointers device.
+ */
+int nvfp4_codec_selftest(int which, const float *in_f32, const uint16_t *in_u16, uint8_t *out_u8, int64_t n,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

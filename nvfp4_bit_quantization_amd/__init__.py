@@ -1,0 +1,243 @@
+"""Python binding of libnvfp4.so: NVFP4 quantisation and the NVFP4 GEMM on
+MI355X (gfx950).
+
+The functions named like the C ABI (``nvfp4_quantize``, ``nvfp4_dequantize``,
+``nvfp4_gemm``, ...) only marshal arguments: torch supplies device memory and
+the current HIP stream, every step of the computation runs in the library's
+HIP kernels.  Importing this package fails loudly when the library has not
+been built (``python -m nvfp4_bit_quantization_amd.build``); there is no CPU
+fallback.
+
+Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1 elements
+in 16-element blocks, E4M3 block scales, an FP32 per-tensor scale, 1D blocks
+for activations/gradients and 16x16 blocks for weights, stochastic rounding for
+gradients, 16x16 random Hadamard transforms on Wgrad inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+# enums (include/nvfp4.h)
+NVFP4_OK = 0
+ROW_1D, COL_1D, TWO_D, TWO_D_T = 0, 1, 2, 3
+RTN, SR = 0, 1
+SCALE_1D16, SCALE_2D16 = 0, 1
+F32, BF16 = 0, 1
+LAYOUTS = {"row": ROW_1D, "col": COL_1D, "2d": TWO_D, "2d_t": TWO_D_T}
+ROUNDINGS = {"rtn": RTN, "sr": SR}
+
+
+class Nvfp4Error(RuntimeError):
+    pass
+
+
+class nvfp4_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p),
+                ("amax", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("scale_kind", ctypes.c_int32), ("rht", ctypes.c_int32)]
+
+
+class nvfp4_quant_output(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("rounding", ctypes.c_int32), ("rht", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
+                ("out", nvfp4_tensor)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libnvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libnvfp4.so is not built: run `python -m nvfp4_bit_quantization_amd.build` "
+                          "(expected at %s)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(nvfp4_quant_output), i32, P, ctypes.c_size_t, P]
+    L.nvfp4_workspace_bytes.restype = ctypes.c_size_t
+    L.nvfp4_workspace_bytes.argtypes = []
+    L.nvfp4_dequantize.restype = i32
+    L.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_tensor), P, i64, P]
+    L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm.argtypes = [ctypes.POINTER(nvfp4_tensor), ctypes.POINTER(nvfp4_tensor), P, ctypes.c_int32, i64, P]
+    L.nvfp4_rht_sign_mask.restype = ctypes.c_uint16
+    L.nvfp4_rht_sign_mask.argtypes = [ctypes.c_uint64]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_status_string.argtypes = [i32]
+    L.nvfp4_codec_selftest.restype = i32
+    L.nvfp4_codec_selftest.argtypes = [i32, P, P, P, i64, P]
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != NVFP4_OK:
+        raise Nvfp4Error("%s failed: %d (%s)" % (what, status, lib().nvfp4_status_string(status).decode()))
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# quantised tensors held in torch device memory
+# ---------------------------------------------------------------------------
+@dataclass
+class QTensor:
+    codes: "object"         # torch.uint8 [rows][cols/2]
+    scales: "object"        # torch.uint8, 1D [rows][cols/16] or 2D [rows/16][cols/16]
+    global_scale: "object"  # torch.float32 [1]
+    amax: "object"          # torch.float32 [1]
+    rows: int
+    cols: int
+    scale_kind: int
+    rht: int = 0
+
+    def c_struct(self) -> nvfp4_tensor:
+        return nvfp4_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale.data_ptr(),
+                            self.amax.data_ptr(), self.rows, self.cols, self.scale_kind, self.rht)
+
+
+def empty_qtensor(rows: int, cols: int, scale_kind: int, device="cuda", rht: int = 0) -> QTensor:
+    import torch
+    sshape = (rows, cols // 16) if scale_kind == SCALE_1D16 else (rows // 16, cols // 16)
+    return QTensor(codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                   scales=torch.empty(sshape, dtype=torch.uint8, device=device),
+                   global_scale=torch.empty(1, dtype=torch.float32, device=device),
+                   amax=torch.empty(1, dtype=torch.float32, device=device),
+                   rows=rows, cols=cols, scale_kind=scale_kind, rht=rht)
+
+
+@dataclass
+class QuantSpec:
+    """One requested output of nvfp4_quantize."""
+    layout: int = ROW_1D
+    rounding: int = RTN
+    rht: bool = False
+    sr_seed: int = 0
+    rht_seed: int = 0
+
+    @staticmethod
+    def of(layout="row", rounding="rtn", rht=False, sr_seed=0, rht_seed=0) -> "QuantSpec":
+        return QuantSpec(LAYOUTS.get(layout, layout), ROUNDINGS.get(rounding, rounding), bool(rht), sr_seed, rht_seed)
+
+
+def output_shape(rows: int, cols: int, layout: int):
+    """(rows, cols, scale_kind) of the stored output for an input [rows][cols]."""
+    if layout == ROW_1D:
+        return rows, cols, SCALE_1D16
+    if layout == COL_1D:
+        return cols, rows, SCALE_1D16
+    if layout == TWO_D:
+        return rows, cols, SCALE_2D16
+    if layout == TWO_D_T:
+        return cols, rows, SCALE_2D16
+    raise ValueError(layout)
+
+
+def new_workspace(device="cuda"):
+    import torch
+    return torch.empty(lib().nvfp4_workspace_bytes() // 4, dtype=torch.float32, device=device)
+
+
+# ---------------------------------------------------------------------------
+# C ABI entry points (argument marshalling only)
+# ---------------------------------------------------------------------------
+def nvfp4_quantize(x, specs: Sequence[QuantSpec], outs: Sequence[QTensor], workspace, stream=None) -> List[QTensor]:
+    """Quantise the bf16 device tensor x [rows][cols] (row stride x.stride(0))
+    into 1 or 2 outputs (see include/nvfp4.h)."""
+    assert len(specs) == len(outs) and 1 <= len(specs) <= 2
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    arr = (nvfp4_quant_output * len(specs))()
+    for i, (s, o) in enumerate(zip(specs, outs)):
+        arr[i] = nvfp4_quant_output(s.layout, s.rounding, int(s.rht), 0, s.sr_seed, s.rht_seed, o.c_struct())
+    st = lib().nvfp4_quantize(ctypes.c_void_p(x.data_ptr()), x.shape[0], x.shape[1], x.stride(0), arr, len(specs),
+                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    _check(st, "nvfp4_quantize")
+    return list(outs)
+
+
+def nvfp4_dequantize(q: QTensor, y, stream=None):
+    """y[r][c] = (e(code) * s_b) / S for the stored orientation of q (fp32)."""
+    import torch
+    assert y.dtype == torch.float32 and y.stride(1) == 1
+    t = q.c_struct()
+    _check(lib().nvfp4_dequantize(ctypes.byref(t), ctypes.c_void_p(y.data_ptr()), y.stride(0), _stream(stream)),
+           "nvfp4_dequantize")
+    return y
+
+
+def nvfp4_gemm(a: QTensor, b: QTensor, c, stream=None):
+    """C[M][N] = A^ B^T / (S_A S_B) into the fp32 or bf16 device tensor c."""
+    import torch
+    dt = F32 if c.dtype == torch.float32 else BF16 if c.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("c must be float32 or bfloat16")
+    assert c.stride(1) == 1
+    ta, tb = a.c_struct(), b.c_struct()
+    _check(lib().nvfp4_gemm(ctypes.byref(ta), ctypes.byref(tb), ctypes.c_void_p(c.data_ptr()), dt, c.stride(0),
+                            _stream(stream)), "nvfp4_gemm")
+    return c
+
+
+def nvfp4_workspace_bytes() -> int:
+    return lib().nvfp4_workspace_bytes()
+
+
+def nvfp4_rht_sign_mask(seed: int) -> int:
+    return lib().nvfp4_rht_sign_mask(seed)
+
+
+def nvfp4_status_string(status: int) -> str:
+    return lib().nvfp4_status_string(status).decode()
+
+
+def nvfp4_codec_selftest(which: int, x, u16, out, stream=None):
+    p = (lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0))
+    _check(lib().nvfp4_codec_selftest(which, p(x), p(u16), p(out), out.numel(), _stream(stream)),
+           "nvfp4_codec_selftest")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# conveniences (allocation + one call)
+# ---------------------------------------------------------------------------
+def quantize(x, specs: Sequence[QuantSpec], workspace=None, stream=None) -> List[QTensor]:
+    """Allocate the outputs for `specs` and quantise x into them."""
+    if workspace is None:
+        workspace = new_workspace(x.device)
+    outs = []
+    for s in specs:
+        r, c, k = output_shape(x.shape[0], x.shape[1], s.layout)
+        outs.append(empty_qtensor(r, c, k, x.device, rht=int(s.rht)))
+    return nvfp4_quantize(x, specs, outs, workspace, stream)
+
+
+def dequantize(q: QTensor, stream=None):
+    import torch
+    y = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
+    return nvfp4_dequantize(q, y, stream)
+
+
+def gemm(a: QTensor, b: QTensor, out_dtype="f32", stream=None):
+    import torch
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
+    return nvfp4_gemm(a, b, c, stream)

@@ -1,0 +1,266 @@
+// C ABI of libnvfp4.so: argument validation on the host, then kernel launches
+// on the caller's stream.  The entry points and their contracts are declared
+// and documented in include/nvfp4.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "nvfp4.h"
+#include "nvfp4_kernels.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+// Philox4x32-10 on the host, for the RHT sign mask (same published algorithm
+// as the device copy: Salmon et al., SC'11).
+uint32_t host_philox_word0(uint64_t seed, const uint32_t ctr_in[4]) {
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool sync_check_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = getenv("NVFP4_SYNC_CHECK");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+int finish(hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) return NVFP4_E_HIP;
+  if (sync_check_enabled()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return NVFP4_E_HIP;
+    if (hipGetLastError() != hipSuccess) return NVFP4_E_HIP;
+  }
+  return NVFP4_OK;
+}
+
+struct OutPlan {
+  int geom;
+  bool rht, sr;
+  int amax_mode;
+};
+
+// validate one output descriptor against the input shape; fill its plan
+int plan_output(const nvfp4_quant_output &o, int64_t R, int64_t C, OutPlan *p) {
+  if (o.reserved != 0) return NVFP4_E_UNSUPPORTED;
+  if (o.rounding != NVFP4_RTN && o.rounding != NVFP4_SR) return NVFP4_E_UNSUPPORTED;
+  if (o.rht != 0 && o.rht != 1) return NVFP4_E_UNSUPPORTED;
+  const nvfp4_tensor &t = o.out;
+  if (!t.codes || !t.scales || !t.global_scale || !t.amax) return NVFP4_E_NULL;
+  if (!aligned16(t.codes)) return NVFP4_E_ALIGN;
+  int64_t rows, cols;
+  int kind;
+  switch (o.layout) {
+    case NVFP4_ROW_1D: p->geom = G_ROW; rows = R; cols = C; kind = NVFP4_SCALE_1D16; break;
+    case NVFP4_COL_1D: p->geom = G_COL; rows = C; cols = R; kind = NVFP4_SCALE_1D16; break;
+    case NVFP4_2D: p->geom = G_TILE; rows = R; cols = C; kind = NVFP4_SCALE_2D16; break;
+    case NVFP4_2D_T: p->geom = G_TILE_T; rows = C; cols = R; kind = NVFP4_SCALE_2D16; break;
+    default: return NVFP4_E_UNSUPPORTED;
+  }
+  if (o.rht && (p->geom == G_TILE || p->geom == G_TILE_T)) return NVFP4_E_UNSUPPORTED;
+  if (t.rows != rows || t.cols != cols || t.scale_kind != kind) return NVFP4_E_SHAPE;
+  p->rht = o.rht != 0;
+  p->sr = o.rounding == NVFP4_SR;
+  p->amax_mode = !p->rht ? AM_PLAIN : (p->geom == G_COL ? AM_RHT_COL : AM_RHT_ROW);
+  return NVFP4_OK;
+}
+
+OutArgs out_args(const nvfp4_quant_output &o, int amax_mode) {
+  OutArgs a;
+  a.codes = o.out.codes;
+  a.scales = o.out.scales;
+  a.S_out = o.out.global_scale;
+  a.amax_out = o.out.amax;
+  a.sr_seed = o.sr_seed;
+  a.amax_mode = amax_mode;
+  a.pad = 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_workspace_bytes(void) { return sizeof(float) * 3 * (size_t)kMaxParts; }
+
+uint16_t nvfp4_rht_sign_mask(uint64_t rht_seed) {
+  const uint32_t ctr[4] = {0u, 0u, 1u, 0u};
+  return (uint16_t)(host_philox_word0(rht_seed, ctr) & 0xFFFFu);
+}
+
+const char *nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_E_NULL: return "a required pointer is NULL";
+    case NVFP4_E_SHAPE: return "size <= 0, not a multiple of 16, or inconsistent with the layout";
+    case NVFP4_E_LD: return "leading dimension smaller than the row length";
+    case NVFP4_E_ALIGN: return "pointer not 16-byte aligned or leading dimension not a multiple of 8";
+    case NVFP4_E_UNSUPPORTED: return "unsupported combination of arguments";
+    case NVFP4_E_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
+                   int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!x || !outs) return NVFP4_E_NULL;
+  if (n_outs != 1 && n_outs != 2) return NVFP4_E_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || (rows % 16) || (cols % 16)) return NVFP4_E_SHAPE;
+  if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31) return NVFP4_E_SHAPE;
+  if (ld_x < cols) return NVFP4_E_LD;
+  if (!aligned16(x) || (ld_x % 8)) return NVFP4_E_ALIGN;
+  if (!workspace) return NVFP4_E_WORKSPACE;
+  if (workspace_bytes < nvfp4_workspace_bytes()) return NVFP4_E_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_E_ALIGN;
+
+  OutPlan p[2];
+  for (int i = 0; i < n_outs; ++i) {
+    const int st = plan_output(outs[i], rows, cols, &p[i]);
+    if (st != NVFP4_OK) return st;
+  }
+  int order[2] = {0, 1};
+  uint32_t mask_rows = 0, mask_cols = 0;
+  if (n_outs == 2) {
+    // canonical pair order: ROW before COL, TILE before TILE_T
+    if ((p[0].geom == G_COL && p[1].geom == G_ROW) || (p[0].geom == G_TILE_T && p[1].geom == G_TILE)) {
+      order[0] = 1;
+      order[1] = 0;
+    }
+    const int g0 = p[order[0]].geom, g1 = p[order[1]].geom;
+    if (!((g0 == G_ROW && g1 == G_COL) || (g0 == G_TILE && g1 == G_TILE_T))) return NVFP4_E_UNSUPPORTED;
+  }
+  for (int i = 0; i < n_outs; ++i) {
+    if (!p[i].rht) continue;
+    const uint32_t m = nvfp4_rht_sign_mask(outs[i].rht_seed);
+    if (p[i].geom == G_COL)
+      mask_rows = m;
+    else
+      mask_cols = m;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const int tiles = quant_tiles(rows, cols);
+  const int nparts = tiles < kMaxParts ? tiles : kMaxParts;
+  float *partials = (float *)workspace;
+
+  AmaxArgs aa;
+  aa.x = (const uint16_t *)x;
+  aa.R = rows;
+  aa.C = cols;
+  aa.ld = ld_x;
+  aa.partials = partials;
+  aa.mask_rows = mask_rows;
+  aa.mask_cols = mask_cols;
+  bool plain = false, rc = false, rr = false;
+  for (int i = 0; i < n_outs; ++i) {
+    plain |= p[i].amax_mode == AM_PLAIN;
+    rc |= p[i].amax_mode == AM_RHT_COL;
+    rr |= p[i].amax_mode == AM_RHT_ROW;
+  }
+  hipError_t e = launch_amax(aa, plain, rc, rr, nparts, s);
+  if (e != hipSuccess) return NVFP4_E_HIP;
+
+  QuantArgs qa;
+  qa.x = (const uint16_t *)x;
+  qa.R = rows;
+  qa.C = cols;
+  qa.ld = ld_x;
+  qa.partials = partials;
+  qa.nparts = nparts;
+  qa.mask_rows = mask_rows;
+  qa.mask_cols = mask_cols;
+  const OutPlan &p0 = p[order[0]];
+  qa.o[0] = out_args(outs[order[0]], p0.amax_mode);
+  OutPlan p1 = {G_NONE, false, false, AM_PLAIN};
+  if (n_outs == 2) {
+    p1 = p[order[1]];
+    qa.o[1] = out_args(outs[order[1]], p1.amax_mode);
+  } else {
+    qa.o[1] = qa.o[0];
+  }
+  bool supported = true;
+  e = launch_quantize(qa, p0.geom, p0.rht, p0.sr, p1.geom, p1.rht, p1.sr, s, &supported);
+  if (!supported) return NVFP4_E_UNSUPPORTED;
+  return finish(e, s);
+}
+
+int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream) {
+  if (!q || !y || !q->codes || !q->scales || !q->global_scale) return NVFP4_E_NULL;
+  if (q->rows <= 0 || q->cols <= 0 || (q->rows % 16) || (q->cols % 16)) return NVFP4_E_SHAPE;
+  if (q->scale_kind != NVFP4_SCALE_1D16 && q->scale_kind != NVFP4_SCALE_2D16) return NVFP4_E_UNSUPPORTED;
+  if (ld_y < q->cols) return NVFP4_E_LD;
+  if (!aligned16(y) || (ld_y % 4) || !aligned16(q->codes)) return NVFP4_E_ALIGN;
+  DequantArgs a;
+  a.codes = q->codes;
+  a.scales = q->scales;
+  a.S = q->global_scale;
+  a.y = y;
+  a.rows = q->rows;
+  a.cols = q->cols;
+  a.ld_y = ld_y;
+  a.scale_kind = q->scale_kind;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_dequantize(a, s), s);
+}
+
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *stream) {
+  if (!a || !b || !c) return NVFP4_E_NULL;
+  if (!a->codes || !a->scales || !a->global_scale || !b->codes || !b->scales || !b->global_scale) return NVFP4_E_NULL;
+  if (a->rows <= 0 || b->rows <= 0 || a->cols <= 0 || (a->rows % 16) || (b->rows % 16) || (a->cols % 16))
+    return NVFP4_E_SHAPE;
+  if (a->cols != b->cols) return NVFP4_E_UNSUPPORTED;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_E_UNSUPPORTED;
+  if ((a->scale_kind != NVFP4_SCALE_1D16 && a->scale_kind != NVFP4_SCALE_2D16) ||
+      (b->scale_kind != NVFP4_SCALE_1D16 && b->scale_kind != NVFP4_SCALE_2D16))
+    return NVFP4_E_UNSUPPORTED;
+  if (ldc < b->rows) return NVFP4_E_LD;
+  if (!aligned16(a->codes) || !aligned16(b->codes) || !aligned16(c)) return NVFP4_E_ALIGN;
+  if (a->rows > ((int64_t)1 << 31) || b->rows > ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+  GemmArgs g;
+  g.a_codes = a->codes;
+  g.a_scales = a->scales;
+  g.a_S = a->global_scale;
+  g.b_codes = b->codes;
+  g.b_scales = b->scales;
+  g.b_S = b->global_scale;
+  g.c = c;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->cols;
+  g.ldc = ldc;
+  g.a_kind = a->scale_kind;
+  g.b_kind = b->scale_kind;
+  g.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_gemm(g, s), s);
+}
+
+int nvfp4_codec_selftest(int which, const float *in_f32, const uint16_t *in_u16, uint8_t *out_u8, int64_t n,
+                         void *stream) {
+  if (which < 0 || which > 2) return NVFP4_E_UNSUPPORTED;
+  if (n < 0) return NVFP4_E_SHAPE;
+  if (n > 0 && (!in_f32 || !out_u8 || (which == 1 && !in_u16))) return NVFP4_E_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_codec_selftest(which, in_f32, in_u16, out_u8, n, s), s);
+}
+
+}  // extern "C"

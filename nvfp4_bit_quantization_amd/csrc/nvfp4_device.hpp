@@ -1,0 +1,146 @@
+// Device helpers for the NVFP4 kernels (gfx950): bf16 unpacking, the E4M3
+// block-scale codec, the E2M1 element encoders, Philox4x32-10 and the 16-point
+// Hadamard butterfly.
+//
+// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1 elements
+// in 16-element blocks, E4M3 block scales, FP32 per-tensor scale, stochastic
+// rounding for gradients, 16x16 random Hadamard transforms on Wgrad inputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// element k (0..7) of 8 bf16 packed in a uint4
+__device__ __forceinline__ float bf16_at(const uint4 &q, int k) {
+  uint32_t w = (k >> 1) == 0 ? q.x : (k >> 1) == 1 ? q.y : (k >> 1) == 2 ? q.z : q.w;
+  return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// ---------------------------------------------------------------- E4M3 ----
+// OCP E4M3FN, nearest-even, saturating at 448, subnormals m * 2^-9 kept.
+// s must be finite and >= 0.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (s >= 448.0f) return 0x7Eu;
+  if (s < 0.015625f) {  // below the smallest normal 2^-6: multiples of 2^-9
+    return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, then RNE
+  }
+  uint32_t u = __float_as_uint(s);
+  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
+  return (u >> 20) - (120u << 3);    // rebias the exponent 127 -> 7
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// ---------------------------------------------------------------- E2M1 ----
+// Nearest-even onto {0,.5,1,1.5,2,3,4,6}, saturating, sign kept: the gfx950
+// conversion instruction with a unit scale (its scale operand only contributes
+// an exponent; with 1.0 it is the plain conversion).  Two values -> one byte
+// (first value in the low nibble) placed in byte `sel` of `old`.
+#define NVFP4_CVT_PK_FP4(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
+
+// Stochastic rounding with a 16-bit uniform: a' = min(|y|, 6) lies between grid
+// neighbours lo <= a' <= hi; round up iff u16 < 65536 * (a' - lo) / (hi - lo).
+// For a' >= 1 the grid points are the binary32 values with one mantissa bit,
+// so lo is a' with the low 22 mantissa bits cleared and the fraction is those
+// bits / 2^22.  Below 1 the spacing is 1/2: frac = 2a' - floor(2a').
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
+  uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
+  float a = fminf(fabsf(y), 6.0f);
+  uint32_t code;
+  if (a >= 1.0f) {
+    uint32_t u = __float_as_uint(a);
+    code = (u >> 22) - 252u + (((u16 << 6) < (u & 0x3FFFFFu)) ? 1u : 0u);
+  } else {
+    float t = a * 2.0f;
+    float fl = __builtin_floorf(t);
+    float fr = t - fl;
+    code = (uint32_t)fl + (((float)u16 < fr * 65536.0f) ? 1u : 0u);
+  }
+  return code | sign;
+}
+
+// -------------------------------------------------------------- Philox ----
+// Philox4x32-10 (Salmon et al., SC'11).  c[] in: counter, out: 4 random words.
+__device__ __forceinline__ void philox4x32_10(uint32_t k0, uint32_t k1, uint32_t c[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[1] = (uint32_t)p1;
+    c[3] = (uint32_t)p0;
+    c[0] = n0;
+    c[2] = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// The 8 words of the two Philox draws that serve one 16-element block:
+// draw g = 2*block + half, counter (g lo, g hi, 0, 0).  Element j of the block
+// uses word (j & 7) >> 1 of draw j >> 3, 16-bit half j & 1.
+__device__ __forceinline__ void sr_draw(uint64_t seed, uint64_t block, uint32_t half, uint32_t w[4]) {
+  const uint64_t g = 2u * block + half;
+  w[0] = (uint32_t)g;
+  w[1] = (uint32_t)(g >> 32);
+  w[2] = 0u;
+  w[3] = 0u;
+  philox4x32_10((uint32_t)seed, (uint32_t)(seed >> 32), w);
+}
+
+__device__ __forceinline__ uint32_t u16_of(const uint32_t w[4], int k) {  // k = j & 7
+  const uint32_t word = (k >> 1) == 0 ? w[0] : (k >> 1) == 1 ? w[1] : (k >> 1) == 2 ? w[2] : w[3];
+  return (k & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// ------------------------------------------------------------ Hadamard ----
+// In-place 16-point fast Walsh-Hadamard transform in binary64 (Sylvester
+// order: out_i = sum_j (-1)^popcount(i&j) in_j).  With bf16 inputs every
+// partial sum is exact while the 16 inputs span fewer than 41 binades.
+__device__ __forceinline__ void fwht16(double v[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const double a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- lanes ------
+// value of lane (lane ^ 8) -- rotate by 8 inside each row of 16 lanes
+__device__ __forceinline__ float swap8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+}
+__device__ __forceinline__ double swap8(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x128, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), 0x128, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// ------------------------------------------------------------- XCDs -------
+// Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works
+// on one contiguous range of tiles (neighbouring tiles share its L2).
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t n) {
+  const uint32_t per = n / 8u, rem = n % 8u, x = b % 8u, i = b / 8u;
+  return x < rem ? x * (per + 1u) + i : rem * (per + 1u) + (x - rem) * per + i;
+}
+
+}  // namespace nvfp4

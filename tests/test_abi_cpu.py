@@ -1,0 +1,138 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/nvfp4.h declares, and rejects invalid arguments on the host before
+anything is enqueued (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import nvfp4_bit_quantization_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        from nvfp4_bit_quantization_amd import build
+        build.build()
+    return nv.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(nvfp4_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_workspace_bytes", "nvfp4_rht_sign_mask",
+              "nvfp4_status_string", "nvfp4_codec_selftest"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", nv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on the error paths
+
+
+def _tensor(rows, cols, kind, codes=FAKE):
+    return nv.nvfp4_tensor(codes, FAKE, FAKE, FAKE, rows, cols, kind, 0)
+
+
+def _out(layout, rows, cols, kind, rounding=0, rht=0, reserved=0, codes=FAKE):
+    return nv.nvfp4_quant_output(layout, rounding, rht, reserved, 1, 2, _tensor(rows, cols, kind, codes))
+
+
+def _q(L, outs, x=FAKE, rows=64, cols=32, ld=32, ws=FAKE, wsb=None):
+    arr = (nv.nvfp4_quant_output * max(1, len(outs)))(*outs)
+    if wsb is None:
+        wsb = L.nvfp4_workspace_bytes()
+    return L.nvfp4_quantize(ctypes.c_void_p(x), rows, cols, ld, arr, len(outs), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_quantize_argument_validation(L):
+    row = _out(nv.ROW_1D, 64, 32, nv.SCALE_1D16)
+    col = _out(nv.COL_1D, 32, 64, nv.SCALE_1D16)
+    assert _q(L, [row], x=0) == -1                                    # NULL x
+    assert _q(L, [row], rows=24) == -2                                 # rows % 16
+    assert _q(L, [row], cols=0) == -2
+    assert _q(L, [row], ld=16) == -3                                   # ld < cols
+    assert _q(L, [row], x=FAKE + 8) == -4                              # misaligned x
+    assert _q(L, [row], ld=36) == -4                                   # ld % 8
+    assert _q(L, [row, col, row]) == -5                                # n_outs
+    assert _q(L, [row], ws=0) == -6
+    assert _q(L, [row], wsb=16) == -6
+    assert _q(L, [_out(nv.TWO_D, 64, 32, nv.SCALE_2D16, rht=1)]) == -5  # RHT with 2D
+    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, rounding=7)]) == -5
+    assert _q(L, [_out(9, 64, 32, nv.SCALE_1D16)]) == -5
+    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, reserved=1)]) == -5
+    assert _q(L, [_out(nv.ROW_1D, 32, 64, nv.SCALE_1D16)]) == -2        # descriptor shape mismatch
+    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_2D16)]) == -2        # wrong scale kind
+    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, codes=0)]) == -1
+    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, codes=FAKE + 4)]) == -4
+    assert _q(L, [row, row]) == -5                                     # unsupported pair
+    assert _q(L, [_out(nv.TWO_D, 64, 32, nv.SCALE_2D16), col]) == -5
+
+
+def test_dequantize_and_gemm_validation(L):
+    t = _tensor(64, 32, nv.SCALE_1D16)
+    y = ctypes.c_void_p(FAKE)
+    assert L.nvfp4_dequantize(None, y, 32, None) == -1
+    assert L.nvfp4_dequantize(ctypes.byref(t), None, 32, None) == -1
+    assert L.nvfp4_dequantize(ctypes.byref(_tensor(60, 32, 0)), y, 32, None) == -2
+    assert L.nvfp4_dequantize(ctypes.byref(t), y, 16, None) == -3
+    assert L.nvfp4_dequantize(ctypes.byref(t), ctypes.c_void_p(FAKE + 4), 32, None) == -4
+    assert L.nvfp4_dequantize(ctypes.byref(_tensor(64, 32, 5)), y, 32, None) == -5
+    a = _tensor(64, 32, nv.SCALE_1D16)
+    b = _tensor(48, 32, nv.SCALE_2D16)
+    bk = _tensor(48, 48, nv.SCALE_1D16)
+    c = ctypes.c_void_p(FAKE)
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(bk), c, 0, 48, None) == -5   # K mismatch
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 3, 48, None) == -5    # dtype
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 40, None) == -3    # ldc < N
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), None, 0, 48, None) == -1
+    assert L.nvfp4_gemm(ctypes.byref(_tensor(64, 40, 0)), ctypes.byref(_tensor(48, 40, 0)), c, 0, 48, None) == -2
+    assert L.nvfp4_codec_selftest(3, None, None, None, 0, None) == -5
+    assert L.nvfp4_codec_selftest(0, None, None, None, -1, None) == -2
+    assert L.nvfp4_codec_selftest(0, None, None, None, 5, None) == -1
+
+
+def test_status_strings(L):
+    for s in range(-7, 1):
+        assert nv.nvfp4_status_string(s)
+    assert nv.nvfp4_status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes_is_small(L):
+    assert 0 < nv.nvfp4_workspace_bytes() <= 64 * 1024
+
+
+def test_rht_sign_mask_matches_oracle(L):
+    import oracle
+    for seed in (0, 1, 1234, 4321, 2**40 + 3, 2**64 - 1):
+        assert nv.nvfp4_rht_sign_mask(seed) == oracle.rht_sign_mask(seed)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(nv, "_lib", None)
+    with pytest.raises(ImportError):
+        nv.lib()

@@ -1,0 +1,100 @@
+"""The device encoders against the oracle's codecs.
+
+The E2M1 round-to-nearest path uses gfx950's FP32->FP4 conversion instruction,
+so it is checked exhaustively over all 2^32 binary32 bit patterns (NaN/Inf
+excluded).  The E4M3 block-scale encoder and the stochastic-rounding encoder
+are software; they are checked on dense samples that include every E4M3
+value, every midpoint and their neighbours, and on structured (y, u16) grids.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_util import host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_bit_quantization_amd as nv
+    nv.lib()
+    return nv
+
+
+def test_e2m1_rtn_exhaustive(nv):
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    pool = ThreadPoolExecutor(16)
+    sub = 1 << 24
+    for start in range(0, 1 << 32, chunk):
+        say("e2m1 exhaustive chunk", hex(start))
+        bits = torch.arange(start, start + chunk, dtype=torch.int64, device="cuda").to(torch.int32)
+        x = bits.view(torch.float32)
+        nv.nvfp4_codec_selftest(0, x, None, out)
+        got = host(out)
+        del bits, x
+        parts = list(pool.map(lambda s: oracle.e2m1_encode_rtn_bits(s, sub), range(start, start + chunk, sub)))
+        want = np.concatenate(parts)
+        finite = want != 0xFF
+        bad = np.flatnonzero((got != want) & finite)
+        assert bad.size == 0, "first mismatching pattern 0x%08x: gpu %x oracle %x" % (
+            start + bad[0], got[bad[0]], want[bad[0]])
+
+
+def test_e4m3_encoder_dense(nv):
+    vals = np.array([oracle.e4m3_value(c) for c in range(0x7F)], dtype=np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids, [448.0, 448.5, 464.0, 479.9, 480.0, 1e3, 1e30, 3.4e38]]).astype(np.float32)
+    nb = [pts]
+    up, dn = pts.copy(), pts.copy()
+    for _ in range(4):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(0))
+        nb += [up.copy(), dn.copy()]
+    lo = int(np.float32(2.0 ** -14).view(np.uint32))
+    hi = int(np.float32(512.0).view(np.uint32))
+    dense = np.arange(lo, hi, 37, dtype=np.uint32).view(np.float32)
+    tiny = np.arange(0, lo, 1 << 10, dtype=np.uint32).view(np.float32)
+    xs = np.concatenate(nb + [dense, tiny]).astype(np.float32)
+    xs = xs[np.isfinite(xs) & (xs >= 0)]
+    say("e4m3 dense", xs.size)
+    x = torch.from_numpy(xs).cuda()
+    out = torch.empty(xs.size, dtype=torch.uint8, device="cuda")
+    nv.nvfp4_codec_selftest(2, x, None, out)
+    got = host(out)
+    want = oracle.e4m3_encode(xs)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (xs[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_e2m1_sr_encoder(nv):
+    rng = np.random.default_rng(1)
+    n = 1 << 22
+    y = np.concatenate([rng.uniform(-7, 7, n // 2).astype(np.float32),
+                        rng.integers(0, 2 ** 32, n // 2, dtype=np.uint64).astype(np.uint32).view(np.float32)])
+    y = y[np.isfinite(y)]
+    u = rng.integers(0, 65536, y.size, dtype=np.uint16)
+    # structured: every u16 against values at and around grid points and midpoints
+    grid = np.array([0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 6.5], np.float32)
+    gpts = np.concatenate([grid, np.nextafter(grid, np.float32(9)), np.nextafter(grid, np.float32(-1)),
+                           grid * np.float32(1.37), np.float32([1e-40, 3e-39, 0.1])])
+    gpts = np.concatenate([gpts, -gpts])
+    ys = np.concatenate([y, np.repeat(gpts, 65536)]).astype(np.float32)
+    us = np.concatenate([u, np.tile(np.arange(65536, dtype=np.uint16), gpts.size)])
+    say("e2m1 sr", ys.size)
+    out = torch.empty(ys.size, dtype=torch.uint8, device="cuda")
+    x = torch.from_numpy(ys).cuda()
+    uu = torch.from_numpy(us.view(np.int16)).cuda()
+    nv.nvfp4_codec_selftest(1, x, uu, out)
+    got = host(out)
+    want = oracle.e2m1_encode_sr(ys, us)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (ys[bad[:5]], us[bad[:5]], got[bad[:5]], want[bad[:5]])
