@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+Default workload (``wgrad_8192x5120``): one step = quantise dY (8192x5120 bf16,
+Laplace(0,1e-3)) column-wise with the 16x16 RHT and stochastic rounding,
+quantise X (8192x5120, N(0,1)) column-wise with the RHT and RTN, and the NVFP4
+weight-gradient GEMM dW = dY^T X (5120x5120, K = 8192, fp32 out).  This is the
+workload on which both halves of the metric (quantise GB/s, Wgrad GEMM
+TFLOP/s) are quoted.  Other workloads (``--workload``): ``act_8192x5120``
+(row + column quantise of an activation), ``weight_5120x20480`` (2D + 2D_T),
+``tiny_256`` and ``linear_step_16384`` (Fprop/Dgrad/Wgrad of a 5120/20480
+two-layer FFN over 16384 tokens).
+
+Prints ONE JSON line.  ``value`` is whole-step throughput (GEMM flops of the
+step over the wall time per step, inputs resident in HBM); per-call times come
+from HIP events recorded on the stream the library launches on.  The
+``roofline`` object is for the dominant kernel; ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def qbytes(rows, cols, outs=1):
+    """Algorithmic bytes of one quantise call: one bf16 read + codes + scales of each output."""
+    n = rows * cols
+    return 2 * n + outs * (n // 2 + n // 16)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "nvfp4_bit_quantization_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary for this
+    kernel, if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, kernel_tag + "_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", txt)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != src_hash:
+        return None
+    return float(t.group(1))
+
+
+class Timer:
+    """HIP events around library calls on the current stream."""
+
+    def __init__(self):
+        self.marks = {}
+
+    def run(self, name, fn):
+        import torch
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.marks.setdefault(name, []).append((s, e))
+
+    def ms(self, name):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.marks[name]]))
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns (step(timer), info dict)
+# ---------------------------------------------------------------------------
+def setup_wgrad(nv, syn, tokens=8192, hidden=5120):
+    import torch
+    dy_bits, x_bits = syn.wgrad_8192x5120(tokens, hidden)
+    dy, x = dev_bf16(dy_bits), dev_bf16(x_bits)
+    ws = nv.new_workspace()
+    s_dy = [nv.QuantSpec.of("col", "sr", True, 1234, 1234)]
+    s_x = [nv.QuantSpec.of("col", "rtn", True, 0, 1234)]
+    q_dy = [nv.empty_qtensor(hidden, tokens, nv.SCALE_1D16, rht=1)]
+    q_x = [nv.empty_qtensor(hidden, tokens, nv.SCALE_1D16, rht=1)]
+    c = torch.empty((hidden, hidden), dtype=torch.float32, device="cuda")
+    flops = 2.0 * hidden * hidden * tokens
+
+    def step(t: Timer):
+        t.run("quantize_dY", lambda: nv.nvfp4_quantize(dy, s_dy, q_dy, ws))
+        t.run("quantize_X", lambda: nv.nvfp4_quantize(x, s_x, q_x, ws))
+        t.run("gemm_wgrad", lambda: nv.nvfp4_gemm(q_dy[0], q_x[0], c))
+
+    info = dict(flops=flops, calls={
+        "quantize_dY": dict(kind="quantize", bytes=qbytes(tokens, hidden)),
+        "quantize_X": dict(kind="quantize", bytes=qbytes(tokens, hidden)),
+        "gemm_wgrad": dict(kind="gemm", flops=flops, M=hidden, N=hidden, K=tokens)},
+        dominant="gemm_wgrad", config=dict(workload="wgrad_8192x5120", tokens=tokens, hidden=hidden,
+                                           quantize="dY col1D+RHT+SR(seed 1234), X col1D+RHT+RTN, RHT seed 1234",
+                                           gemm="dW = dY^T X, M=N=%d, K=%d, fp32 out" % (hidden, tokens)))
+    return step, info
+
+
+def setup_act(nv, syn):
+    bits = syn.act_8192x5120()
+    x = dev_bf16(bits)
+    ws = nv.new_workspace()
+    specs = [nv.QuantSpec.of("row"), nv.QuantSpec.of("col")]
+    outs = [nv.empty_qtensor(8192, 5120, 0), nv.empty_qtensor(5120, 8192, 0)]
+
+    def step(t):
+        t.run("quantize_act_row_col", lambda: nv.nvfp4_quantize(x, specs, outs, ws))
+
+    return step, dict(flops=0.0, calls={"quantize_act_row_col": dict(kind="quantize", bytes=qbytes(8192, 5120, 2))},
+                      dominant="quantize_act_row_col",
+                      config=dict(workload="act_8192x5120", quantize="row1D + col1D RTN from one read"))
+
+
+def setup_weight(nv, syn):
+    bits = syn.weight_5120x20480()
+    x = dev_bf16(bits)
+    ws = nv.new_workspace()
+    specs = [nv.QuantSpec.of("2d"), nv.QuantSpec.of("2d_t")]
+    outs = [nv.empty_qtensor(5120, 20480, 1), nv.empty_qtensor(20480, 5120, 1)]
+    n = 5120 * 20480
+    b = 2 * n + 2 * (n // 2 + n // 256)
+
+    def step(t):
+        t.run("quantize_weight_2d", lambda: nv.nvfp4_quantize(x, specs, outs, ws))
+
+    return step, dict(flops=0.0, calls={"quantize_weight_2d": dict(kind="quantize", bytes=b)},
+                      dominant="quantize_weight_2d",
+                      config=dict(workload="weight_5120x20480", quantize="2D 16x16 RTN + transposed copy"))
+
+
+def setup_tiny(nv, syn):
+    bits = syn.tiny_256()
+    x = dev_bf16(bits)
+    ws = nv.new_workspace()
+    specs = [nv.QuantSpec.of("row")]
+    outs = [nv.empty_qtensor(256, 256, 0)]
+    import torch
+    y = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+
+    def step(t):
+        t.run("quantize_tiny", lambda: nv.nvfp4_quantize(x, specs, outs, ws))
+        t.run("dequantize_tiny", lambda: nv.nvfp4_dequantize(outs[0], y))
+
+    return step, dict(flops=0.0, calls={"quantize_tiny": dict(kind="quantize", bytes=qbytes(256, 256)),
+                                        "dequantize_tiny": dict(kind="quantize", bytes=256 * 256 * (4 + 0.5625))},
+                      dominant="quantize_tiny", config=dict(workload="tiny_256"))
+
+
+def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
+    import torch
+    d = syn.linear_step_16384(tokens, hidden, ffn)
+    X, W1, W2, dY = (dev_bf16(d[k]) for k in ("X", "W1", "W2", "dY"))
+    del d
+    ws = nv.new_workspace()
+    bf, f32 = torch.bfloat16, torch.float32
+    H = torch.empty((tokens, ffn), dtype=bf, device="cuda")
+    Y = torch.empty((tokens, hidden), dtype=bf, device="cuda")
+    dH = torch.empty((tokens, ffn), dtype=bf, device="cuda")
+    dX = torch.empty((tokens, hidden), dtype=bf, device="cuda")
+    dW1 = torch.empty((ffn, hidden), dtype=f32, device="cuda")
+    dW2 = torch.empty((hidden, ffn), dtype=f32, device="cuda")
+    E = nv.empty_qtensor
+    qX = [E(tokens, hidden, 0), E(hidden, tokens, 0, rht=1)]
+    qW1 = [E(ffn, hidden, 1), E(hidden, ffn, 1)]
+    qH = [E(tokens, ffn, 0), E(ffn, tokens, 0, rht=1)]
+    qW2 = [E(hidden, ffn, 1), E(ffn, hidden, 1)]
+    qdY = [E(tokens, hidden, 0), E(hidden, tokens, 0, rht=1)]
+    qdH = [E(tokens, ffn, 0), E(ffn, tokens, 0, rht=1)]
+    S = nv.QuantSpec.of
+    sX = [S("row"), S("col", "rtn", True, 0, 4321)]
+    sW = [S("2d"), S("2d_t")]
+    sdY = [S("row", "sr", False, 1234), S("col", "sr", True, 1235, 4321)]
+    sdH = [S("row", "sr", False, 1236), S("col", "sr", True, 1237, 4321)]
+    g = 2.0 * tokens * ffn * hidden
+
+    def step(t):
+        t.run("q_X", lambda: nv.nvfp4_quantize(X, sX, qX, ws))
+        t.run("q_W1", lambda: nv.nvfp4_quantize(W1, sW, qW1, ws))
+        t.run("fprop_H", lambda: nv.nvfp4_gemm(qX[0], qW1[0], H))
+        t.run("q_H", lambda: nv.nvfp4_quantize(H, sX, qH, ws))
+        t.run("q_W2", lambda: nv.nvfp4_quantize(W2, sW, qW2, ws))
+        t.run("fprop_Y", lambda: nv.nvfp4_gemm(qH[0], qW2[0], Y))
+        t.run("q_dY", lambda: nv.nvfp4_quantize(dY, sdY, qdY, ws))
+        t.run("dgrad_dH", lambda: nv.nvfp4_gemm(qdY[0], qW2[1], dH))
+        t.run("q_dH", lambda: nv.nvfp4_quantize(dH, sdH, qdH, ws))
+        t.run("dgrad_dX", lambda: nv.nvfp4_gemm(qdH[0], qW1[1], dX))
+        t.run("wgrad_dW2", lambda: nv.nvfp4_gemm(qdY[1], qH[1], dW2))
+        t.run("wgrad_dW1", lambda: nv.nvfp4_gemm(qdH[1], qX[1], dW1))
+
+    calls = {
+        "q_X": dict(kind="quantize", bytes=qbytes(tokens, hidden, 2)),
+        "q_W1": dict(kind="quantize", bytes=2 * ffn * hidden + 2 * (ffn * hidden // 2 + ffn * hidden // 256)),
+        "fprop_H": dict(kind="gemm", flops=g), "q_H": dict(kind="quantize", bytes=qbytes(tokens, ffn, 2)),
+        "q_W2": dict(kind="quantize", bytes=2 * ffn * hidden + 2 * (ffn * hidden // 2 + ffn * hidden // 256)),
+        "fprop_Y": dict(kind="gemm", flops=g), "q_dY": dict(kind="quantize", bytes=qbytes(tokens, hidden, 2)),
+        "dgrad_dH": dict(kind="gemm", flops=g), "q_dH": dict(kind="quantize", bytes=qbytes(tokens, ffn, 2)),
+        "dgrad_dX": dict(kind="gemm", flops=g), "wgrad_dW2": dict(kind="gemm", flops=g),
+        "wgrad_dW1": dict(kind="gemm", flops=g)}
+    return step, dict(flops=6 * g, calls=calls, dominant="wgrad_dW2",
+                      config=dict(workload="linear_step_16384", tokens=tokens, hidden=hidden, ffn=ffn,
+                                  step="Fprop H,Y; Dgrad dH,dX; Wgrad dW2,dW1; 6 quantise calls"))
+
+
+WORKLOADS = {"wgrad_8192x5120": setup_wgrad, "act_8192x5120": setup_act, "weight_5120x20480": setup_weight,
+             "tiny_256": setup_tiny, "linear_step_16384": setup_linear}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the workload
+# ---------------------------------------------------------------------------
+def cpu_baseline(workload: str, syn):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    if workload == "wgrad_8192x5120":
+        tokens, cols = 8192, 1280
+        dy = syn.laplace(tokens, cols, 404, 1e-3)
+        xx = syn.normal(tokens, cols, 405)
+        t0 = time.perf_counter()
+        qa = oracle.quantize(dy, "col", "sr", True, 1234, 1234)
+        qb = oracle.quantize(xx, "col", "rtn", True, 0, 1234)
+        t1 = time.perf_counter()
+        oracle.gemm_f64(qa, qb)
+        t2 = time.perf_counter()
+        flops = 2.0 * cols * cols * tokens
+        return dict(value=flops / (t2 - t0) / 1e12, unit="TFLOP/s", cores=blas_threads, kind="oracle",
+                    sample="Wgrad path on an 8192x1280 slice of dY and X (1/4 of hidden): C oracle quantise "
+                           "(col+RHT, SR/RTN; 1 thread, %.2f s) + binary64 GEMM 1280x1280x8192 (BLAS, %d threads, "
+                           "%.2f s)" % (t1 - t0, blas_threads, t2 - t1))
+    if workload in ("act_8192x5120", "weight_5120x20480", "tiny_256"):
+        if workload == "act_8192x5120":
+            bits, specs = syn.act_8192x5120(2048, 5120), ["row", "col"]
+            nbytes = qbytes(2048, 5120, 2)
+        elif workload == "weight_5120x20480":
+            bits, specs = syn.weight_5120x20480(1280, 20480), ["2d", "2d_t"]
+            nbytes = 2 * bits.size + 2 * (bits.size // 2 + bits.size // 256)
+        else:
+            bits, specs = syn.tiny_256(), ["row"]
+            nbytes = qbytes(256, 256)
+        t0 = time.perf_counter()
+        for s in specs:
+            oracle.quantize(bits, s)
+        dt = time.perf_counter() - t0
+        return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                    sample="%s quantise of a %dx%d slice (single-threaded C oracle, %.2f s)" % (
+                        "+".join(specs), bits.shape[0], bits.shape[1], dt))
+    # linear step: one Wgrad GEMM + its two quantisations on a 1/8 token slice
+    tokens, hidden, ffn = 2048, 5120, 2560
+    dy = syn.laplace(tokens, hidden, 504, 1e-3)
+    h = syn.normal(tokens, ffn, 501)
+    t0 = time.perf_counter()
+    qa = oracle.quantize(dy, "col", "sr", True, 1235, 4321)
+    qb = oracle.quantize(h, "col", "rtn", True, 0, 4321)
+    oracle.gemm_f64(qa, qb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * hidden * ffn * tokens
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=blas_threads, kind="oracle",
+                sample="dW2 slice: 2048 tokens, 5120x2560 Wgrad with both column quantisations (%.2f s)" % dt)
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wgrad_8192x5120", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="run a plain device copy of N MiB (for scaling the HBM byte counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_bit_quantization_amd as nv
+    from nvfp4_bit_quantization_amd import synthetic as syn
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes per copy" % n)
+        return
+    nv.lib()
+    log("setting up", args.workload)
+    step, info = WORKLOADS[args.workload](nv, syn)
+    torch.cuda.synchronize()
+
+    warm = Timer()
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    t = Timer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
+
+    parts = {}
+    for name, c in info["calls"].items():
+        ms = t.ms(name)
+        if c["kind"] == "gemm":
+            tf = c["flops"] / (ms * 1e-3) / 1e12
+            parts[name] = dict(ms=round(ms, 4), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
+        else:
+            gbs = c["bytes"] / (ms * 1e-3) / 1e9
+            parts[name] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+
+    dom = info["dominant"]
+    dc = info["calls"][dom]
+    dms = t.ms(dom)
+    if dc["kind"] == "gemm":
+        achieved = dc["flops"] / (dms * 1e-3) / 1e12
+        src = source_hash("gemm.hip", "nvfp4_device.hpp")
+        traffic = read_traffic("gemm_" + args.workload, src)
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4), traffic=traffic, kernel="gemm_kernel<4,4>",
+                    ms=round(dms, 4), source_hash=src)
+    else:
+        achieved = dc["bytes"] / (dms * 1e-3) / 1e9
+        src = source_hash("quantize.hip", "nvfp4_device.hpp")
+        traffic = read_traffic("quantize_" + args.workload, src)
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel="amax+quantize pass",
+                    ms=round(dms, 4), source_hash=src)
+
+    if info["flops"] > 0:
+        value = info["flops"] / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    else:
+        value = sum(c["bytes"] for c in info["calls"].values() if c["kind"] == "quantize") / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+    qcalls = [n for n, c in info["calls"].items() if c["kind"] == "quantize"]
+    quant = None
+    if qcalls:
+        qb = sum(info["calls"][n]["bytes"] for n in qcalls)
+        qms = sum(t.ms(n) for n in qcalls)
+        quant = dict(gbs=round(qb / (qms * 1e-3) / 1e9, 1), frac_hbm=round(qb / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     bytes=qb, ms=round(qms, 4))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a sample)")
+        cpu = cpu_baseline(args.workload, syn)
+
+    out = {
+        "metric": "NVFP4 quantize GB/s (% HBM peak); NVFP4 Wgrad GEMM TFLOP/s (% MFMA peak)",
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 operands; fp32/fp64 quantise math; fp16 MFMA, fp32 accumulate", "data": "synthetic",
+        "config": info["config"], "quantize": quant, "calls": parts, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,8 @@
 #include "nvfp4_device.hpp"
 #include "nvfp4_kernels.hpp"
 
+#include <stdlib.h>
+
 namespace nvfp4 {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -128,7 +130,7 @@ __device__ __forceinline__ void stage_store(uint8_t *lcodes, uint32_t *lscales, 
 }
 
 template <int TM, int TN>
-__global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kGThreads) void gemm_generic_kernel(GemmArgs g) {
   constexpr int BM = GemmTile<TM, TN>::BM, BN = GemmTile<TM, TN>::BN, ROWS = GemmTile<TM, TN>::ROWS;
   __shared__ __attribute__((aligned(16))) uint8_t lcodes[2][ROWS * kRowBytes];
   __shared__ uint32_t lscales[2][ROWS];
@@ -223,11 +225,247 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs g) {
     }
 }
 
+// ===========================================================================
+// Fast path (M, N multiples of 256, K a multiple of 128): 256x256x128 tiles,
+// three LDS stages filled by direct global->LDS transfers.
+//
+// LDS stage layout (36 KiB): codes of the 256 A rows then the 256 B rows,
+// 64 bytes (one 128-wide K slice) per row in four 16-byte chunks stored in
+// the order chunk ^ swz(row), then 8 scale bytes per row as two dwords stored
+// in the order half ^ ((row >> 4) & 1).  The swizzles make the fragment reads
+// (ds_read_b128 of one row per lane, ds_read_b32 of its scales) free of bank
+// conflicts for 32- and 64-bank LDS.  The transfers write consecutive 16-byte
+// (4-byte for scales) slots per lane, so the swizzle is applied by choosing
+// which global chunk each lane fetches.
+//
+// K mapping inside a 128-wide K-tile: lane-half h of the MFMA in sub-step s
+// (0..7) holds k = 64h + 8s + [0, 8): dword s of the 32 bytes at byte 32h of
+// the row slice, under block scale 4h + s/2 (byte s/2 of scale dword h).
+// ===========================================================================
+constexpr int kFBK = 128;
+constexpr int kFStageCodes = 512 * 64;         // bytes of codes per stage
+constexpr int kFStageBytes = kFStageCodes + 512 * 8;
+constexpr int kFStages = 3;
+
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(size_t)(lds_void_t *)p; }
+
+// one wave-wide direct transfer: lane l's 16 (4) bytes at base + voff land at
+// LDS byte lds + 16 l (4 l)
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// vmcnt <= n (other counters untouched)
+#define NVFP4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+struct FastCtx {
+  // per-lane global offsets (bytes) of this lane's 8 code chunks and 4 scale dwords at kt = 0
+  uint32_t coff[8];
+  uint32_t soff[4];
+};
+
+// `wave` must be wave-uniform (an SGPR): each wave issues exactly 12 transfers
+// per K-tile, which the vmcnt waits of the main loop count on.
+__device__ __forceinline__ void fast_issue(const GemmArgs &g, const FastCtx &c, uint32_t lds_stage, int64_t kt,
+                                           uint32_t wave) {
+  const uint32_t kcode = (uint32_t)kt * 64u, kscale = (uint32_t)kt * 8u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_stage + (wave * 8 + i) * 1024u);
+    if (wave * 8 + i < 16)  // slots 0..1023 hold A rows
+      dma16(g.a_codes, c.coff[i] + kcode, lds);
+    else
+      dma16(g.b_codes, c.coff[i] + kcode, lds);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_stage + kFStageCodes + (wave * 4 + i) * 256u);
+    if (wave * 4 + i < 8)  // scale slots 0..511 hold A rows
+      dma4(g.a_scales, c.soff[i] + kscale, lds);
+    else
+      dma4(g.b_scales, c.soff[i] + kscale, lds);
+  }
+}
+
+template <int TM, int TN>
+__global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
+  static_assert(TM == 4 && TN == 4, "fast path is laid out for 256x256 tiles");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFStages * kFStageBytes];
+
+  const int64_t tiles_n = g.N / 256;
+  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(tile / tiles_n) * 256;
+  const int64_t n0 = (int64_t)(tile % tiles_n) * 256;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lr = lane & 31, h = lane >> 5;
+  const uint32_t kbytes = (uint32_t)(g.K / 2), kblocks = (uint32_t)(g.K / 16);
+
+  // which global bytes this lane transfers (the same for every K-tile up to the K offset)
+  FastCtx c;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t q = (wave * 8 + i) * 64 + lane;  // 16-byte slot of the stage
+    const uint32_t row = q >> 2;                      // 0..511: A rows then B rows
+    const uint32_t chunk = (q & 3u) ^ swz(row);
+    const uint32_t grow = (uint32_t)(row < 256 ? m0 + row : n0 + (row - 256));
+    c.coff[i] = grow * kbytes + chunk * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t d = (wave * 4 + i) * 64 + lane;  // scale dword slot
+    const uint32_t row = d >> 1;
+    const uint32_t half = (d & 1u) ^ ((row >> 4) & 1u);
+    const uint32_t grow = (uint32_t)(row < 256 ? m0 + row : n0 + (row - 256));
+    const int kind = row < 256 ? g.a_kind : g.b_kind;
+    const uint32_t srow = kind == 0 ? grow : (grow >> 4);
+    c.soff[i] = srow * kblocks + half * 4u;
+  }
+
+  float16v acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const uint32_t lds0 = lds_addr(lds);
+  const int64_t KT = g.K / kFBK;
+  fast_issue(g, c, lds0, 0, wave);
+  if (KT > 1) fast_issue(g, c, lds0 + kFStageBytes, 1, wave);
+
+  // LDS byte offsets (within a stage) of this lane's fragments
+  uint32_t aoff[TM][2], boff[TN][2], asoff[TM], bsoff[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const uint32_t r = wm * 128 + i * 32 + lr;
+    aoff[i][0] = (r * 4 + ((2 * h) ^ swz(r))) * 16;
+    aoff[i][1] = (r * 4 + ((2 * h + 1) ^ swz(r))) * 16;
+    asoff[i] = kFStageCodes + (r * 2 + (h ^ ((r >> 4) & 1u))) * 4;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const uint32_t r = 256 + wn * 128 + j * 32 + lr;
+    boff[j][0] = (r * 4 + ((2 * h) ^ swz(r))) * 16;
+    boff[j][1] = (r * 4 + ((2 * h + 1) ^ swz(r))) * 16;
+    bsoff[j] = kFStageCodes + (r * 2 + (h ^ ((r >> 4) & 1u))) * 4;
+  }
+
+  int stage = 0;
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT)
+      NVFP4_WAIT_VMCNT(12);  // this wave's transfers of tile kt are done (tile kt+1's may be in flight)
+    else
+      NVFP4_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; stage (kt+2)%3 is no longer read
+    asm volatile("" ::: "memory");
+    if (kt + 2 < KT) {
+      const int st2 = stage >= 1 ? stage - 1 : 2;  // (kt + 2) % 3
+      fast_issue(g, c, lds0 + st2 * kFStageBytes, kt + 2, wave);
+    }
+    const uint8_t *base = lds + stage * kFStageBytes;
+    uint4 qa[TM][2], qb[TN][2];
+    uint32_t sa[TM], sb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      qa[i][0] = *reinterpret_cast<const uint4 *>(base + aoff[i][0]);
+      qa[i][1] = *reinterpret_cast<const uint4 *>(base + aoff[i][1]);
+      sa[i] = *reinterpret_cast<const uint32_t *>(base + asoff[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      qb[j][0] = *reinterpret_cast<const uint4 *>(base + boff[j][0]);
+      qb[j][1] = *reinterpret_cast<const uint4 *>(base + boff[j][1]);
+      sb[j] = *reinterpret_cast<const uint32_t *>(base + bsoff[j]);
+    }
+    // E4M3 scales -> fp16 pairs: lo = blocks (4h, 4h+1), hi = (4h+2, 4h+3)
+    half2v sal[TM], sah[TM], sbl[TN], sbh[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      sal[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, false);
+      sah[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, true);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      sbl[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[j], 1.0f, false);
+      sbh[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[j], 1.0f, true);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      half8v fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint4 &q = qa[i][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+        const half2v sp = (s >> 2) == 0 ? sal[i] : sah[i];
+        fa[i] = expand8(w, ((s >> 1) & 1) ? sp[1] : sp[0]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint4 &q = qb[j][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+        const half2v sp = (s >> 2) == 0 ? sbl[j] : sbh[j];
+        fb[j] = expand8(w, ((s >> 1) & 1) ? sp[1] : sp[0]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    stage = stage == 2 ? 0 : stage + 1;
+  }
+
+  // epilogue: C = acc / (S_A S_B), 32-bit offsets from the tile origin
+  const float inv = 1.0f / (*g.a_S * *g.b_S);
+  const uint32_t ldc = (uint32_t)g.ldc;
+  if (g.c_bf16) {
+    uint16_t *ct = reinterpret_cast<uint16_t *>(g.c) + m0 * g.ldc + n0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          const uint32_t n = wn * 128 + j * 32 + lr;
+          const uint32_t u = __float_as_uint(acc[i][j][r] * inv);
+          ct[m * ldc + n] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        }
+  } else {
+    float *ct = reinterpret_cast<float *>(g.c) + m0 * g.ldc + n0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          const uint32_t n = wn * 128 + j * 32 + lr;
+          ct[m * ldc + n] = acc[i][j][r] * inv;
+        }
+  }
+}
+
+bool gemm_fast_ok(const GemmArgs &g) {
+  return g.M % 256 == 0 && g.N % 256 == 0 && g.K % kFBK == 0 && g.K / 2 * (g.M > g.N ? g.M : g.N) < (1ll << 32) &&
+         g.ldc * 256 < (1ll << 31);
+}
+
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   constexpr int TM = 4, TN = 4;
   constexpr int BM = GemmTile<TM, TN>::BM, BN = GemmTile<TM, TN>::BN;
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);
+  if (gemm_fast_ok(g) && !getenv("NVFP4_GEMM_GENERIC"))
+    hipLaunchKernelGGL((gemm_fast_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_generic_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -42,6 +42,11 @@ CASES = [  # (M, N, K, a layout, b layout, out dtype)
     (304, 272, 576, "2d", "row", "f32"),
     (512, 384, 1024, "row", "2d", "bf16"),
     (272, 528, 2048, "row", "row", "f32"),
+    # shapes on the 256x256x128 fast path
+    (256, 256, 128, "row", "row", "f32"),
+    (512, 768, 384, "row", "2d", "bf16"),
+    (768, 512, 1280, "2d", "row", "f32"),
+    (1024, 1024, 2048, "col", "col", "f32"),
 ]
 
 
@@ -62,6 +67,20 @@ def test_gemm_small(nv, case):
     assert err <= 1e-3, err
     if dt == "f32":
         assert err <= 1e-5, err  # fp32 accumulation of exact products
+
+
+def test_fast_and_generic_kernels_agree(nv, monkeypatch):
+    """The 256x256x128 fast path and the generic kernel compute the same sums."""
+    M, N, K = 512, 512, 1024
+    say("gemm fast vs generic")
+    qa = quant(nv, syn.activation(M, K, seed=11), "row")
+    qb = quant(nv, syn.normal(N, K, seed=12, std=0.02), "2d")
+    c_fast = host(nv.gemm(qa, qb, "f32"))
+    torch.cuda.synchronize()
+    monkeypatch.setenv("NVFP4_GEMM_GENERIC", "1")
+    c_gen = host(nv.gemm(qa, qb, "f32"))
+    torch.cuda.synchronize()
+    assert rel_frobenius(c_fast, c_gen) <= 1e-6
 
 
 def test_gemm_ldc_and_zero_operand(nv):
