@@ -107,7 +107,7 @@ typedef struct {
  * Defines: page paragraph 2 (format, 1D/2D block scaling, stochastic rounding
  * on gradients, RHT on Wgrad inputs).
  *   x          device, bf16, 16-byte aligned, ld_x >= cols, ld_x % 8 == 0
- *   rows, cols multiples of 16
+ *   rows, cols multiples of 16, rows/16 * cols < 2^31
  *   outs       host array of n_outs (1 or 2) output descriptors.  With two
  *              outputs the pair must be {ROW_1D, COL_1D} (either order, any
  *              rounding/RHT each) or {2D, 2D_T}; two outputs sharing RHT

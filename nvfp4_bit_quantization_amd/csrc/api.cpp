@@ -126,6 +126,8 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
   if (n_outs != 1 && n_outs != 2) return NVFP4_E_UNSUPPORTED;
   if (rows <= 0 || cols <= 0 || (rows % 16) || (cols % 16)) return NVFP4_E_SHAPE;
   if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31) return NVFP4_E_SHAPE;
+  // 16-element blocks are numbered in 31 bits (the stochastic-rounding counters)
+  if ((rows / 16) * cols >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
   if (ld_x < cols) return NVFP4_E_LD;
   if (!aligned16(x) || (ld_x % 8)) return NVFP4_E_ALIGN;
   if (!workspace) return NVFP4_E_WORKSPACE;

@@ -265,31 +265,68 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t l
 #define NVFP4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 struct FastCtx {
+  const uint8_t *cbase;  // codes of the operand this wave transfers (A: waves 0-1, B: waves 2-3)
+  const uint8_t *sbase;  // its scales
   // per-lane global offsets (bytes) of this lane's 8 code chunks and 4 scale dwords at kt = 0
   uint32_t coff[8];
   uint32_t soff[4];
 };
 
-// `wave` must be wave-uniform (an SGPR): each wave issues exactly 12 transfers
-// per K-tile, which the vmcnt waits of the main loop count on.
-__device__ __forceinline__ void fast_issue(const GemmArgs &g, const FastCtx &c, uint32_t lds_stage, int64_t kt,
-                                           uint32_t wave) {
-  const uint32_t kcode = (uint32_t)kt * 64u, kscale = (uint32_t)kt * 8u;
+// Each wave issues exactly 12 transfers per K-tile (8 x 1 KiB of codes, 4 x
+// 256 B of scales), which the vmcnt waits of the main loop count on.  Waves 0-1
+// fill the A half of the stage (code slots 0..1023, scale slots 0..511), waves
+// 2-3 the B half.  `wave` must be wave-uniform.
+__device__ __forceinline__ void fast_issue(const FastCtx &c, uint32_t lds_stage, uint32_t kt, uint32_t wave) {
+  const uint32_t kcode = kt * 64u, kscale = kt * 8u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_stage + (wave * 8 + i) * 1024u);
-    if (wave * 8 + i < 16)  // slots 0..1023 hold A rows
-      dma16(g.a_codes, c.coff[i] + kcode, lds);
-    else
-      dma16(g.b_codes, c.coff[i] + kcode, lds);
-  }
+  for (int i = 0; i < 8; ++i)
+    dma16(c.cbase, c.coff[i] + kcode, __builtin_amdgcn_readfirstlane(lds_stage + (wave * 8 + i) * 1024u));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma4(c.sbase, c.soff[i] + kscale,
+         __builtin_amdgcn_readfirstlane(lds_stage + kFStageCodes + (wave * 4 + i) * 256u));
+}
+
+// lgkmcnt <= 0 (LDS reads of this wave complete; other counters untouched)
+#define NVFP4_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
+
+// The fp16 MFMA operands of one sub-step (16 k): 4 A and 4 B fragments.
+struct Frags {
+  half8v a[4], b[4];
+};
+
+// Expand sub-step s (0..3) of one half of a K-tile: dword s of this lane's
+// 16 code bytes of each row, under block scale element s/2 of the pair.
+template <int S>
+__device__ __forceinline__ void expand_step(Frags &f, const uint4 qa[4], const uint4 qb[4], const half2v sa[4],
+                                            const half2v sb[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_stage + kFStageCodes + (wave * 4 + i) * 256u);
-    if (wave * 4 + i < 8)  // scale slots 0..511 hold A rows
-      dma4(g.a_scales, c.soff[i] + kscale, lds);
-    else
-      dma4(g.b_scales, c.soff[i] + kscale, lds);
+    const uint32_t w = S == 0 ? qa[i].x : S == 1 ? qa[i].y : S == 2 ? qa[i].z : qa[i].w;
+    f.a[i] = expand8(w, (S >> 1) ? sa[i][1] : sa[i][0]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = S == 0 ? qb[j].x : S == 1 ? qb[j].y : S == 2 ? qb[j].z : qb[j].w;
+    f.b[j] = expand8(w, (S >> 1) ? sb[j][1] : sb[j][0]);
+  }
+}
+
+__device__ __forceinline__ void mfma_step(float16v acc[4][4], const Frags &f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Instruction order of one sub-step: each MFMA followed by four VALU
+// instructions of the next sub-step's expansion (64 of them per 16 MFMAs), so
+// the expansion runs in the shadow of the 8-pass MFMAs instead of between them.
+__device__ __forceinline__ void interleave_step() {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
   }
 }
 
@@ -309,6 +346,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
 
   // which global bytes this lane transfers (the same for every K-tile up to the K offset)
   FastCtx c;
+  c.cbase = wave < 2 ? g.a_codes : g.b_codes;
+  c.sbase = wave < 2 ? g.a_scales : g.b_scales;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t q = (wave * 8 + i) * 64 + lane;  // 16-byte slot of the stage
@@ -336,12 +375,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const uint32_t lds0 = lds_addr(lds);
-  const int64_t KT = g.K / kFBK;
-  fast_issue(g, c, lds0, 0, wave);
-  if (KT > 1) fast_issue(g, c, lds0 + kFStageBytes, 1, wave);
-
-  // LDS byte offsets (within a stage) of this lane's fragments
+  // LDS byte offsets (within a stage) of this lane's fragments: [i][0] holds
+  // the k of the first half of the K-tile (sub-steps 0-3), [i][1] the second
   uint32_t aoff[TM][2], boff[TN][2], asoff[TM], bsoff[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -358,69 +393,128 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     bsoff[j] = kFStageCodes + (r * 2 + (h ^ ((r >> 4) & 1u))) * 4;
   }
 
-  int stage = 0;
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT)
-      NVFP4_WAIT_VMCNT(12);  // this wave's transfers of tile kt are done (tile kt+1's may be in flight)
-    else
-      NVFP4_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();  // ... and every wave's; stage (kt+2)%3 is no longer read
-    asm volatile("" ::: "memory");
-    if (kt + 2 < KT) {
-      const int st2 = stage >= 1 ? stage - 1 : 2;  // (kt + 2) % 3
-      fast_issue(g, c, lds0 + st2 * kFStageBytes, kt + 2, wave);
-    }
-    const uint8_t *base = lds + stage * kFStageBytes;
-    uint4 qa[TM][2], qb[TN][2];
-    uint32_t sa[TM], sb[TN];
+  // Pipeline.  Transfers run up to three K-tiles ahead of the MFMAs; every
+  // iteration issues exactly one tile's transfers (the index clamped to the
+  // last tile, so the vmcnt bookkeeping is the same in every iteration; the
+  // clamped copies land in stages nobody reads again).  The barrier of tile
+  // kt+1 sits between the two halves of tile kt, and the fp16 fragments are
+  // expanded one MFMA sub-step ahead, so MFMAs are ready on both sides of it.
+  const uint32_t lds0 = lds_addr(lds);
+  const uint32_t KT = (uint32_t)(g.K / kFBK), klast = KT - 1;
+  fast_issue(c, lds0, 0, wave);
+  fast_issue(c, lds0 + kFStageBytes, klast < 1 ? klast : 1, wave);
+  fast_issue(c, lds0 + 2 * kFStageBytes, klast < 2 ? klast : 2, wave);
+  NVFP4_WAIT_VMCNT(24);  // this wave's transfers of tile 0 are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // first-half codes and the tile's scales (E4M3 -> fp16 pairs: lo = blocks
+  // (4h, 4h+1) of the first half, hi = (4h+2, 4h+3) of the second)
+  uint4 qlo_a[TM], qlo_b[TN];
+  half2v sal[TM], sah[TM], sbl[TN], sbh[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      qa[i][0] = *reinterpret_cast<const uint4 *>(base + aoff[i][0]);
-      qa[i][1] = *reinterpret_cast<const uint4 *>(base + aoff[i][1]);
-      sa[i] = *reinterpret_cast<const uint32_t *>(base + asoff[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      qb[j][0] = *reinterpret_cast<const uint4 *>(base + boff[j][0]);
-      qb[j][1] = *reinterpret_cast<const uint4 *>(base + boff[j][1]);
-      sb[j] = *reinterpret_cast<const uint32_t *>(base + bsoff[j]);
-    }
-    // E4M3 scales -> fp16 pairs: lo = blocks (4h, 4h+1), hi = (4h+2, 4h+3)
-    half2v sal[TM], sah[TM], sbl[TN], sbh[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      sal[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, false);
-      sah[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[i], 1.0f, true);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      sbl[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[j], 1.0f, false);
-      sbh[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[j], 1.0f, true);
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8v fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint4 &q = qa[i][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        const half2v sp = (s >> 2) == 0 ? sal[i] : sah[i];
-        fa[i] = expand8(w, ((s >> 1) & 1) ? sp[1] : sp[0]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint4 &q = qb[j][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        const half2v sp = (s >> 2) == 0 ? sbl[j] : sbh[j];
-        fb[j] = expand8(w, ((s >> 1) & 1) ? sp[1] : sp[0]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    stage = stage == 2 ? 0 : stage + 1;
+  for (int i = 0; i < TM; ++i) {
+    qlo_a[i] = *reinterpret_cast<const uint4 *>(lds + aoff[i][0]);
+    const uint32_t sw = *reinterpret_cast<const uint32_t *>(lds + asoff[i]);
+    sal[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+    sah[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
   }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    qlo_b[j] = *reinterpret_cast<const uint4 *>(lds + boff[j][0]);
+    const uint32_t sw = *reinterpret_cast<const uint32_t *>(lds + bsoff[j]);
+    sbl[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+    sbh[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
+  }
+  Frags f, fn;
+  expand_step<0>(f, qlo_a, qlo_b, sal, sbl);
+
+  uint32_t stage = 0;
+  for (uint32_t kt = 0; kt < KT; ++kt) {
+    // Each sub-step is a scheduling region of its own (sched_barrier), in
+    // which the MFMAs of one sub-step interleave with the expansion of the next.
+    const uint8_t *base = lds + stage * kFStageBytes;
+    uint4 qhi_a[TM], qhi_b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) qhi_a[i] = *reinterpret_cast<const uint4 *>(base + aoff[i][1]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) qhi_b[j] = *reinterpret_cast<const uint4 *>(base + boff[j][1]);
+
+    // first half: sub-steps 0-3 (sub-step 0's fragments are ready)
+    expand_step<1>(fn, qlo_a, qlo_b, sal, sbl);
+    mfma_step(acc, f);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the second-half code reads first
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+    expand_step<2>(f, qlo_a, qlo_b, sal, sbl);
+    mfma_step(acc, fn);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+    expand_step<3>(fn, qlo_a, qlo_b, sal, sbl);
+    mfma_step(acc, f);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+    expand_step<0>(f, qhi_a, qhi_b, sah, sbh);
+    mfma_step(acc, fn);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+
+    half2v cah[TM], cbh[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) cah[i] = sah[i];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) cbh[j] = sbh[j];
+
+    NVFP4_WAIT_LGKM0();    // this wave's reads of the stage are complete
+    NVFP4_WAIT_VMCNT(12);  // this wave's transfers of tile kt+1 are done (kt+2's may be in flight)
+    __builtin_amdgcn_s_barrier();  // every wave's: tile kt+1 is in LDS, this stage is free
+    asm volatile("" ::: "memory");
+    fast_issue(c, lds_addr(base), kt + 3 < klast ? kt + 3 : klast, wave);
+    const uint32_t nstage = stage == 2 ? 0 : stage + 1;
+    const uint8_t *nbase = lds + nstage * kFStageBytes;
+    uint32_t swa[TM], swb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      qlo_a[i] = *reinterpret_cast<const uint4 *>(nbase + aoff[i][0]);
+      swa[i] = *reinterpret_cast<const uint32_t *>(nbase + asoff[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      qlo_b[j] = *reinterpret_cast<const uint4 *>(nbase + boff[j][0]);
+      swb[j] = *reinterpret_cast<const uint32_t *>(nbase + bsoff[j]);
+    }
+    stage = nstage;
+
+    // second half: sub-steps 4-7, then sub-step 0 of tile kt+1 is expanded
+    // (on the last tile from a stale stage; those fragments are not used)
+    expand_step<1>(fn, qhi_a, qhi_b, cah, cbh);
+    mfma_step(acc, f);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+    expand_step<2>(f, qhi_a, qhi_b, cah, cbh);
+    mfma_step(acc, fn);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+    expand_step<3>(fn, qhi_a, qhi_b, cah, cbh);
+    mfma_step(acc, f);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      sal[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i], 1.0f, false);
+      sah[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i], 1.0f, true);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      sbl[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j], 1.0f, false);
+      sbh[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j], 1.0f, true);
+    }
+    expand_step<0>(f, qlo_a, qlo_b, sal, sbl);
+    mfma_step(acc, fn);
+    interleave_step();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  NVFP4_WAIT_VMCNT(0);  // the clamped transfers of the last iterations
 
   // epilogue: C = acc / (S_A S_B), 32-bit offsets from the tile origin
   const float inv = 1.0f / (*g.a_S * *g.b_S);

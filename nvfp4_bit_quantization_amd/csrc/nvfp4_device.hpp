@@ -26,15 +26,16 @@ __device__ __forceinline__ float bf16_at(const uint4 &q, int k) {
 
 // ---------------------------------------------------------------- E4M3 ----
 // OCP E4M3FN, nearest-even, saturating at 448, subnormals m * 2^-9 kept.
-// s must be finite and >= 0.
+// s must be finite and >= 0.  Branch-free: both the normal and the subnormal
+// encodings are formed and the right one selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  if (s >= 448.0f) return 0x7Eu;
-  if (s < 0.015625f) {  // below the smallest normal 2^-6: multiples of 2^-9
-    return (uint32_t)__builtin_rintf(s * 512.0f);  // exact scaling, then RNE
-  }
-  uint32_t u = __float_as_uint(s);
-  u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit mantissa to 3 bits, ties to even
-  return (u >> 20) - (120u << 3);    // rebias the exponent 127 -> 7
+  const uint32_t u = __float_as_uint(s);
+  // normal range: round the 23-bit mantissa to 3 bits (ties to even), rebias 127 -> 7
+  const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  // below the smallest normal 2^-6: multiples of 2^-9 (exact scaling, then RNE)
+  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
+  const uint32_t c = s < 0.015625f ? sub : normal;
+  return s >= 448.0f ? 0x7Eu : c;
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
@@ -53,21 +54,19 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // neighbours lo <= a' <= hi; round up iff u16 < 65536 * (a' - lo) / (hi - lo).
 // For a' >= 1 the grid points are the binary32 values with one mantissa bit,
 // so lo is a' with the low 22 mantissa bits cleared and the fraction is those
-// bits / 2^22.  Below 1 the spacing is 1/2: frac = 2a' - floor(2a').
+// bits / 2^22 (u16 < d / 64 <=> 64 u16 < d).  Below 1 the spacing is 1/2:
+// frac = 2a' - floor(2a'), every step exact.  Branch-free: both forms are
+// evaluated and the right one selected.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-  uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
-  float a = fminf(fabsf(y), 6.0f);
-  uint32_t code;
-  if (a >= 1.0f) {
-    uint32_t u = __float_as_uint(a);
-    code = (u >> 22) - 252u + (((u16 << 6) < (u & 0x3FFFFFu)) ? 1u : 0u);
-  } else {
-    float t = a * 2.0f;
-    float fl = __builtin_floorf(t);
-    float fr = t - fl;
-    code = (uint32_t)fl + (((float)u16 < fr * 65536.0f) ? 1u : 0u);
-  }
-  return code | sign;
+  const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
+  const float a = fminf(fabsf(y), 6.0f);
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t code_hi = (u >> 22) - 252u + (((u16 << 6) < (u & 0x3FFFFFu)) ? 1u : 0u);
+  const float t = a * 2.0f;
+  const float fl = __builtin_floorf(t);
+  const float fr = t - fl;
+  const uint32_t code_lo = (uint32_t)fl + (((float)u16 < fr * 65536.0f) ? 1u : 0u);
+  return (a >= 1.0f ? code_hi : code_lo) | sign;
 }
 
 // -------------------------------------------------------------- Philox ----
@@ -89,12 +88,12 @@ __device__ __forceinline__ void philox4x32_10(uint32_t k0, uint32_t k1, uint32_t
 }
 
 // The 8 words of the two Philox draws that serve one 16-element block:
-// draw g = 2*block + half, counter (g lo, g hi, 0, 0).  Element j of the block
-// uses word (j & 7) >> 1 of draw j >> 3, 16-bit half j & 1.
-__device__ __forceinline__ void sr_draw(uint64_t seed, uint64_t block, uint32_t half, uint32_t w[4]) {
-  const uint64_t g = 2u * block + half;
-  w[0] = (uint32_t)g;
-  w[1] = (uint32_t)(g >> 32);
+// draw g = 2*block + half, counter (g, 0, 0, 0) -- block indices stay below
+// 2^31 (checked on the host), so the counter's high word is 0.  Element j of
+// the block uses word (j & 7) >> 1 of draw j >> 3, 16-bit half j & 1.
+__device__ __forceinline__ void sr_draw(uint64_t seed, uint32_t block, uint32_t half, uint32_t w[4]) {
+  w[0] = 2u * block + half;
+  w[1] = 0u;
   w[2] = 0u;
   w[3] = 0u;
   philox4x32_10((uint32_t)seed, (uint32_t)(seed >> 32), w);
@@ -133,6 +132,20 @@ __device__ __forceinline__ double swap8(double v) {
   const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x128, 0xF, 0xF, false);
   const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), 0x128, 0xF, 0xF, false);
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// value of lane (lane ^ 1) / (lane ^ 2): DPP quad permutations
+__device__ __forceinline__ uint32_t xor1u(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xor2u(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ float xor1f(float v) { return __uint_as_float(xor1u(__float_as_uint(v))); }
+__device__ __forceinline__ float xor2f(float v) { return __uint_as_float(xor2u(__float_as_uint(v))); }
+__device__ __forceinline__ double xor1d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  return __longlong_as_double((long long)(((uint64_t)xor1u((uint32_t)(u >> 32)) << 32) | xor1u((uint32_t)u)));
+}
+__device__ __forceinline__ double xor2d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  return __longlong_as_double((long long)(((uint64_t)xor2u((uint32_t)(u >> 32)) << 32) | xor2u((uint32_t)u)));
 }
 
 // ------------------------------------------------------------- XCDs -------

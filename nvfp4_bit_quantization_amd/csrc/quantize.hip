@@ -52,25 +52,46 @@ __device__ __forceinline__ float wave_max(float m) {
 }
 
 // ------------------------------------------------------------------------
-// Hadamard helpers on a lane's data
+// RHT: sign vectors as XORs of the bf16 sign bits, then the butterflies
 // ------------------------------------------------------------------------
-// Column j of the micro-tile (16 rows) through the RHT: z_i = 1/4 sum H d v.
-__device__ __forceinline__ void rht_column(const uint4 raw[16], int j, uint32_t mask, double d[16]) {
+// along rows: row i of the 16-row group gets d_i
+__device__ __forceinline__ void flip_rows(uint4 raw[16], uint32_t mask) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float v = bf16_at(raw[i], j);
-    d[i] = (double)(((mask >> i) & 1u) ? -v : v);
+    const uint32_t f = ((mask >> i) & 1u) ? 0x80008000u : 0u;
+    raw[i].x ^= f;
+    raw[i].y ^= f;
+    raw[i].z ^= f;
+    raw[i].w ^= f;
   }
+}
+// along columns: column j = 8 hi + k of the 16-column block gets d_j
+__device__ __forceinline__ void flip_cols(uint4 raw[16], uint32_t mask, uint32_t hi) {
+  const uint32_t m = mask >> (8 * hi);
+  uint32_t f[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) f[p] = (((m >> (2 * p)) & 1u) << 15) | (((m >> (2 * p + 1)) & 1u) << 31);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    raw[i].x ^= f[0];
+    raw[i].y ^= f[1];
+    raw[i].z ^= f[2];
+    raw[i].w ^= f[3];
+  }
+}
+
+// column j (16 rows, signs applied): H v in binary64 (the 1/4 is applied later)
+__device__ __forceinline__ void fwht_column(const uint4 raw[16], int j, double d[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d[i] = (double)bf16_at(raw[i], j);
   fwht16(d);
 }
 
-// Row i of a 16-column block held by lanes l (cols 0..7) and l^8 (cols 8..15).
-__device__ __forceinline__ void rht_row(const uint4 &row, uint32_t hi, uint32_t mask, double d[8]) {
+// row i of a 16-column block held by lanes l (cols 0..7) and l^8 (cols 8..15),
+// signs applied: butterflies on j bits 0-2 inside the lane, bit 3 across lanes
+__device__ __forceinline__ void fwht_row(const uint4 &row, uint32_t hi, double d[8]) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float v = bf16_at(row, k);
-    d[k] = (double)(((mask >> (hi * 8 + k)) & 1u) ? -v : v);
-  }
+  for (int k = 0; k < 8; ++k) d[k] = (double)bf16_at(row, k);
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -82,7 +103,6 @@ __device__ __forceinline__ void rht_row(const uint4 &row, uint32_t hi, uint32_t 
       }
     }
   }
-  // last butterfly stage pairs element k of the left lane with element k of the right lane
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const double other = swap8(d[k]);
@@ -110,19 +130,27 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(AmaxArgs a) {
         for (int k = 0; k < 8; ++k) m_plain = fmaxf(m_plain, fabsf(bf16_at(raw[i], k)));
     }
     if (RC) {
+      uint4 r[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = raw[i];
+      flip_rows(r, a.mask_rows);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         double d[16];
-        rht_column(raw, j, a.mask_rows, d);
+        fwht_column(r, j, d);
 #pragma unroll
         for (int i = 0; i < 16; ++i) m_rc = fmax(m_rc, fabs(d[i]));
       }
     }
     if (RR) {
+      uint4 r[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = raw[i];
+      flip_cols(r, a.mask_cols, L.hi);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         double d[8];
-        rht_row(raw[i], L.hi, a.mask_cols, d);
+        fwht_row(r[i], L.hi, d);
 #pragma unroll
         for (int k = 0; k < 8; ++k) m_rr = fmax(m_rr, fabs(d[k]));
       }
@@ -182,7 +210,7 @@ __device__ __forceinline__ float block_scale(float bmax, float S, const float *l
 // ------------------------------------------------------------------------
 template <int G, bool RHT, bool SR>
 __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane &L, const OutArgs &o, float S,
-                                                const float *lut, uint32_t mask, int64_t R, int64_t C) {
+                                                const float *lut, int64_t R, int64_t C) {
   if (G == G_ROW) {
     const int64_t nbc = C / 16;
 #pragma unroll
@@ -190,7 +218,7 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
       float v[8];
       if (RHT) {
         double d[8];
-        rht_row(raw[i], L.hi, mask, d);
+        fwht_row(raw[i], L.hi, d);
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = (float)(d[k] * 0.25);
       } else {
@@ -204,12 +232,12 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
       uint32_t sc;
       const float rb = block_scale(m, S, lut, &sc);
       const int64_t r = L.r0 + i;
-      const int64_t blk = r * nbc + L.c0 / 16;
+      const uint32_t blk = (uint32_t)(r * nbc + L.c0 / 16);
       if (!L.hi) o.scales[blk] = (uint8_t)sc;
       uint32_t word;
       if (SR) {
         uint32_t w[4];
-        sr_draw(o.sr_seed, (uint64_t)blk, L.hi, w);
+        sr_draw(o.sr_seed, blk, L.hi, w);
         word = pack8_sr(v, rb, w);
       } else {
         word = pack8_rtn(v, rb);
@@ -223,7 +251,7 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
       float v[16];
       if (RHT) {
         double d[16];
-        rht_column(raw, j, mask, d);
+        fwht_column(raw, j, d);
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = (float)(d[i] * 0.25);
       } else {
@@ -236,14 +264,14 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
       uint32_t sc;
       const float rb = block_scale(m, S, lut, &sc);
       const int64_t c = L.c0 + j;
-      const int64_t blk = c * nbr + L.r0 / 16;
+      const uint32_t blk = (uint32_t)(c * nbr + L.r0 / 16);
       o.scales[blk] = (uint8_t)sc;
       uint2 words;
       if (SR) {
         uint32_t w[4];
-        sr_draw(o.sr_seed, (uint64_t)blk, 0u, w);
+        sr_draw(o.sr_seed, blk, 0u, w);
         words.x = pack8_sr(v, rb, w);
-        sr_draw(o.sr_seed, (uint64_t)blk, 1u, w);
+        sr_draw(o.sr_seed, blk, 1u, w);
         words.y = pack8_sr(v + 8, rb, w);
       } else {
         words.x = pack8_rtn(v, rb);
@@ -272,7 +300,7 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
         uint32_t word;
         if (SR) {
           uint32_t w[4];
-          sr_draw(o.sr_seed, (uint64_t)(r * nbc + L.c0 / 16), L.hi, w);
+          sr_draw(o.sr_seed, (uint32_t)(r * nbc + L.c0 / 16), L.hi, w);
           word = pack8_sr(v, rb, w);
         } else {
           word = pack8_rtn(v, rb);
@@ -293,7 +321,7 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             uint32_t w[4];
-            sr_draw(o.sr_seed, (uint64_t)((L.r0 + i) * nbc + L.c0 / 16), L.hi, w);
+            sr_draw(o.sr_seed, (uint32_t)((L.r0 + i) * nbc + L.c0 / 16), L.hi, w);
             const uint32_t code = e2m1_sr(v[i] * rb, u16_of(w, j));
             if (i < 8)
               lo |= code << (4 * i);
@@ -355,11 +383,30 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantArgs a) {
   __syncthreads();
   if (!L.valid) return;
 
-  quantize_output<G0, RHT0, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], G0 == G_COL ? a.mask_rows : a.mask_cols, a.R,
-                                 a.C);
-  if (NOUT == 2)
-    quantize_output<G1, RHT1, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], G1 == G_COL ? a.mask_rows : a.mask_cols,
-                                   a.R, a.C);
+  // outputs without the RHT first, then the RHT ones with their sign vector
+  // XORed into the raw bf16 values
+  if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
+  if (NOUT == 2 && !RHT1) quantize_output<G1, false, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
+  if (RHT0) {
+    if (G0 == G_COL)
+      flip_rows(raw, a.mask_rows);
+    else
+      flip_cols(raw, a.mask_cols, L.hi);
+    quantize_output<G0, true, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
+    if (NOUT == 2 && RHT1) {  // undo
+      if (G0 == G_COL)
+        flip_rows(raw, a.mask_rows);
+      else
+        flip_cols(raw, a.mask_cols, L.hi);
+    }
+  }
+  if (NOUT == 2 && RHT1) {
+    if (G1 == G_COL)
+      flip_rows(raw, a.mask_rows);
+    else
+      flip_cols(raw, a.mask_cols, L.hi);
+    quantize_output<G1, true, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
+  }
 }
 
 // ------------------------------------------------------------------------
