@@ -46,7 +46,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
-               "-fexcess-precision=standard", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+               "-fexcess-precision=standard", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -63,6 +63,7 @@ def _load():
     i64, i32, u64, u32 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32
     f32, f64 = ctypes.c_float, ctypes.c_double
     sig = {
+        "oracle_threads": (i32, []),
         "oracle_e2m1_value": (f64, [ctypes.c_uint8]),
         "oracle_e2m1_encode_rtn": (ctypes.c_uint8, [f32]),
         "oracle_e2m1_encode_sr": (ctypes.c_uint8, [f32, ctypes.c_uint16]),
@@ -101,6 +102,11 @@ def _ptr(a: np.ndarray):
 # --------------------------------------------------------------------------
 # scalar / array codecs
 # --------------------------------------------------------------------------
+def threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
+
+
 def e2m1_value(code: int) -> float:
     return _load().oracle_e2m1_value(code)
 

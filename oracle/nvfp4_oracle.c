@@ -16,8 +16,8 @@
  * formulas; the arithmetic convention below (global scale 448*6/amax, block
  * scale E4M3(amax_b/6 * S), elements scaled onto the E2M1 grid
  * {0,.5,1,1.5,2,3,4,6}) is the fixed convention of this project, and every
- * point the page leaves open is a stated reading (the list of readings is in
- * the design notes at the repository root).
+ * point the page leaves open is a reading of this project, named where the
+ * code takes it.
  *
  * Precision: the page fixes the per-tensor scale as FP32, so the scale chain
  * (S, block scale, per-block factor, scaled element) is evaluated as single
@@ -26,6 +26,10 @@
  * binary64 (exact for 16 bf16 terms whose exponents span fewer than 41
  * binades) and rounded once to binary32.  Grid searches (E2M1, E4M3) compare
  * against exact binary64 midpoints.
+ *
+ * Loops over independent rows or blocks run in parallel (OpenMP); every value
+ * is produced by the same sequence of operations at any thread count, and the
+ * per-tensor maximum does not depend on the order of comparisons.
  *
  * Parity pins: every function here is checked by the tests under tests/
  * against enumeration, brute force, closed forms, a library routine or
@@ -38,6 +42,9 @@
 #include <string.h>
 #include <math.h>
 #include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 
 /* ---- enumerations (the library's C header defines the same numbers) ---- */
@@ -53,6 +60,15 @@
 /* ------------------------------------------------------------------------ */
 /* bf16 / fp32 helpers                                                        */
 /* ------------------------------------------------------------------------ */
+/* Threads the parallel loops use (1 in a build without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 static float bf16_bits_to_float(uint16_t h) {
   uint32_t u = (uint32_t)h << 16; /* bf16 is the top half of a binary32 */
   float f;
@@ -264,6 +280,7 @@ int oracle_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int lay
   size_t n = (size_t)rows * (size_t)cols;
   float *v = (float *)malloc(n * sizeof(float));
   if (!v) return -2;
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c = 0; c < cols; c++)
       v[r * cols + c] = transposed_input ? v_at(x, ld, c, r) : v_at(x, ld, r, c);
@@ -272,6 +289,7 @@ int oracle_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int lay
    * working orientation: hidden for ROW_1D, tokens for COL_1D). */
   if (rht) {
     uint16_t mask = oracle_rht_sign_mask(rht_seed);
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; r++)
       for (int64_t g = 0; g < cols; g += 16) {
         double in[16], z[16];
@@ -283,6 +301,7 @@ int oracle_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int lay
 
   /* Step 3: per-tensor amax and Step 4: the FP32 global (encode) scale. */
   float amax = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : amax)
   for (size_t i = 0; i < n; i++) {
     float a = fabsf(v[i]);
     if (a > amax) amax = a;
@@ -296,6 +315,7 @@ int oracle_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int lay
   int is2d = (layout == OR_2D || layout == OR_2D_T);
   int64_t bh = is2d ? 16 : 1; /* block height in the working orientation */
   int64_t nbc = cols / 16;
+#pragma omp parallel for schedule(static)
   for (int64_t br = 0; br < rows; br += bh)
     for (int64_t bc = 0; bc < nbc; bc++) {
       float amax_b = 0.0f;
@@ -368,6 +388,7 @@ int oracle_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                       float S, float *y) {
   if (rows <= 0 || cols <= 0 || (rows % 16) || (cols % 16)) return -1;
   if (scale_kind != OR_SCALE_1D16 && scale_kind != OR_SCALE_2D16) return -1;
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c = 0; c < cols; c++) {
       float e = (float)oracle_e2m1_value(code_at(codes, cols, r, c));
@@ -383,6 +404,7 @@ int oracle_decode_products(const uint8_t *codes, const uint8_t *scales, int64_t 
                            double *out) {
   if (rows <= 0 || cols <= 0 || (rows % 16) || (cols % 16)) return -1;
   if (scale_kind != OR_SCALE_1D16 && scale_kind != OR_SCALE_2D16) return -1;
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c = 0; c < cols; c++)
       out[r * cols + c] = oracle_e2m1_value(code_at(codes, cols, r, c)) *
@@ -400,6 +422,7 @@ int oracle_gemm_f64(const uint8_t *a_codes, const uint8_t *a_scales, int a_kind,
                     const uint8_t *b_scales, int b_kind, float b_S, int64_t M, int64_t N, int64_t K, double *c) {
   if (M <= 0 || N <= 0 || K <= 0 || (M % 16) || (N % 16) || (K % 16)) return -1;
   double denom = (double)a_S * (double)b_S; /* exact product of two binary32 */
+#pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; m++)
     for (int64_t nn = 0; nn < N; nn++) {
       double acc = 0.0;

@@ -90,6 +90,9 @@ def test_quantize_argument_validation(L):
     assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, codes=FAKE + 4)]) == -4
     assert _q(L, [row, row]) == -5                                     # unsupported pair
     assert _q(L, [_out(nv.TWO_D, 64, 32, nv.SCALE_2D16), col]) == -5
+    # 16-element blocks are numbered in 31 bits: rows/16 * cols < 2^31
+    big_r, big_c = 1 << 20, 1 << 15
+    assert _q(L, [_out(nv.ROW_1D, big_r, big_c, nv.SCALE_1D16)], rows=big_r, cols=big_c, ld=big_c) == -2
 
 
 def test_dequantize_and_gemm_validation(L):

@@ -5,10 +5,11 @@ The per-role recipe follows paragraph 2 of the NVFP4 pretraining news page
 (zubnet.ai): activations 1D round-to-nearest, weights 2D (the transposed copy
 serves Dgrad), gradients 1D with stochastic rounding, and the 16x16 RHT with
 shared signs on both Wgrad inputs.  Hidden 5120 and FFN 20480 are the real
-sizes; the token count is reduced (512) so that the CPU oracle finishes in
-seconds.  Each quantisation is checked against the oracle on the GPU's own
-bf16 input (bit-exact, or the RHT tolerance), each GEMM on 64 sampled output
-rows against the oracle's binary64 product of the GPU's operands.
+sizes; the step runs with 512 tokens and with the full 16384 (the shapes the
+benchmark times).  Each quantisation is checked against the oracle on the
+GPU's own bf16 input (bit-exact, or the RHT tolerance), each GEMM on 64
+sampled output rows against the oracle's binary64 product of the GPU's
+operands.
 """
 import numpy as np
 import pytest
@@ -22,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-T, HID, FFN = 512, 5120, 20480
+HID, FFN = 5120, 20480
 
 
 @pytest.fixture(scope="module")
@@ -58,7 +59,8 @@ def check_gemm(qa, qb, c, what, dt):
     assert err <= 1e-3, (what, err)
 
 
-def test_linear_step_stagewise(nv):
+def run_step(nv, T):
+    say("linear step", T, "tokens")
     d = syn.linear_step_16384(T, HID, FFN)
     dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in d.items()}
     S = nv.QuantSpec.of
@@ -112,3 +114,11 @@ def test_linear_step_stagewise(nv):
     rel = rel_frobenius(host(dW2)[rows], ref)
     say("dW2 vs unquantised product", rel)
     assert rel < 0.2
+
+
+def test_linear_step_stagewise(nv):
+    run_step(nv, 512)
+
+
+def test_linear_step_16384_full(nv):
+    run_step(nv, 16384)
