@@ -275,16 +275,20 @@ struct FastCtx {
 // Each wave issues exactly 12 transfers per K-tile (8 x 1 KiB of codes, 4 x
 // 256 B of scales), which the vmcnt waits of the main loop count on.  Waves 0-1
 // fill the A half of the stage (code slots 0..1023, scale slots 0..511), waves
-// 2-3 the B half.  `wave` must be wave-uniform.
+// 2-3 the B half.  Transfers [FIRST, FIRST + COUNT) of the 12 are issued here
+// (0-7 codes, 8-11 scales), so that a tile's transfers can be spread over
+// several MFMA sub-steps.  `wave` must be wave-uniform.
+template <int FIRST, int COUNT>
 __device__ __forceinline__ void fast_issue(const FastCtx &c, uint32_t lds_stage, uint32_t kt, uint32_t wave) {
   const uint32_t kcode = kt * 64u, kscale = kt * 8u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    dma16(c.cbase, c.coff[i] + kcode, __builtin_amdgcn_readfirstlane(lds_stage + (wave * 8 + i) * 1024u));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma4(c.sbase, c.soff[i] + kscale,
-         __builtin_amdgcn_readfirstlane(lds_stage + kFStageCodes + (wave * 4 + i) * 256u));
+  for (int t = FIRST; t < FIRST + COUNT; ++t) {
+    if (t < 8)
+      dma16(c.cbase, c.coff[t] + kcode, __builtin_amdgcn_readfirstlane(lds_stage + (wave * 8 + t) * 1024u));
+    else
+      dma4(c.sbase, c.soff[t - 8] + kscale,
+           __builtin_amdgcn_readfirstlane(lds_stage + kFStageCodes + (wave * 4 + (t - 8)) * 256u));
+  }
 }
 
 // lgkmcnt <= 0 (LDS reads of this wave complete; other counters untouched)
@@ -396,15 +400,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   // Pipeline.  Transfers run up to three K-tiles ahead of the MFMAs; every
   // iteration issues exactly one tile's transfers (the index clamped to the
   // last tile, so the vmcnt bookkeeping is the same in every iteration; the
-  // clamped copies land in stages nobody reads again).  The barrier of tile
+  // clamped copies land in stages nobody reads again), two per sub-step: the
+  // first six of tile kt+3 after the barrier of iteration kt, the other six
+  // in the first half of iteration kt+1, before its barrier.  The barrier of tile
   // kt+1 sits between the two halves of tile kt, and the fp16 fragments are
   // expanded one MFMA sub-step ahead, so MFMAs are ready on both sides of it.
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t KT = (uint32_t)(g.K / kFBK), klast = KT - 1;
-  fast_issue(c, lds0, 0, wave);
-  fast_issue(c, lds0 + kFStageBytes, klast < 1 ? klast : 1, wave);
-  fast_issue(c, lds0 + 2 * kFStageBytes, klast < 2 ? klast : 2, wave);
-  NVFP4_WAIT_VMCNT(24);  // this wave's transfers of tile 0 are done
+  fast_issue<0, 12>(c, lds0, 0, wave);
+  fast_issue<0, 12>(c, lds0 + kFStageBytes, klast < 1 ? klast : 1, wave);
+  fast_issue<0, 6>(c, lds0 + 2 * kFStageBytes, klast < 2 ? klast : 2, wave);
+  NVFP4_WAIT_VMCNT(18);  // this wave's transfers of tile 0 are done
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
@@ -434,6 +440,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     // Each sub-step is a scheduling region of its own (sched_barrier), in
     // which the MFMAs of one sub-step interleave with the expansion of the next.
     const uint8_t *base = lds + stage * kFStageBytes;
+    const uint32_t pstage = stage == 0 ? 2 : stage - 1;  // (kt + 2) % 3
+    const uint32_t plds = lds0 + pstage * kFStageBytes, ptile = kt + 2 < klast ? kt + 2 : klast;
     uint4 qhi_a[TM], qhi_b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) qhi_a[i] = *reinterpret_cast<const uint4 *>(base + aoff[i][1]);
@@ -445,14 +453,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     mfma_step(acc, f);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the second-half code reads first
     interleave_step();
+    fast_issue<6, 2>(c, plds, ptile, wave);
     __builtin_amdgcn_sched_barrier(0);
     expand_step<2>(f, qlo_a, qlo_b, sal, sbl);
     mfma_step(acc, fn);
     interleave_step();
+    fast_issue<8, 2>(c, plds, ptile, wave);
     __builtin_amdgcn_sched_barrier(0);
     expand_step<3>(fn, qlo_a, qlo_b, sal, sbl);
     mfma_step(acc, f);
     interleave_step();
+    fast_issue<10, 2>(c, plds, ptile, wave);
     __builtin_amdgcn_sched_barrier(0);
     expand_step<0>(f, qhi_a, qhi_b, sah, sbh);
     mfma_step(acc, fn);
@@ -469,7 +480,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     NVFP4_WAIT_VMCNT(12);  // this wave's transfers of tile kt+1 are done (kt+2's may be in flight)
     __builtin_amdgcn_s_barrier();  // every wave's: tile kt+1 is in LDS, this stage is free
     asm volatile("" ::: "memory");
-    fast_issue(c, lds_addr(base), kt + 3 < klast ? kt + 3 : klast, wave);
+    const uint32_t dlds = lds_addr(base), dtile = kt + 3 < klast ? kt + 3 : klast;
     const uint32_t nstage = stage == 2 ? 0 : stage + 1;
     const uint8_t *nbase = lds + nstage * kFStageBytes;
     uint32_t swa[TM], swb[TN];
@@ -490,14 +501,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     expand_step<1>(fn, qhi_a, qhi_b, cah, cbh);
     mfma_step(acc, f);
     interleave_step();
+    fast_issue<0, 2>(c, dlds, dtile, wave);
     __builtin_amdgcn_sched_barrier(0);
     expand_step<2>(f, qhi_a, qhi_b, cah, cbh);
     mfma_step(acc, fn);
     interleave_step();
+    fast_issue<2, 2>(c, dlds, dtile, wave);
     __builtin_amdgcn_sched_barrier(0);
     expand_step<3>(fn, qhi_a, qhi_b, cah, cbh);
     mfma_step(acc, f);
     interleave_step();
+    fast_issue<4, 2>(c, dlds, dtile, wave);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
