@@ -112,8 +112,10 @@ typedef struct {
  *              outputs the pair must be {ROW_1D, COL_1D} (either order, any
  *              rounding/RHT each) or {2D, 2D_T}; two outputs sharing RHT
  *              settings share the amax.
- *   workspace  device scratch of at least nvfp4_workspace_bytes() bytes
- *              (per-workgroup partial maxima; no initialisation needed)
+ *   workspace  device scratch of at least nvfp4_workspace_bytes() bytes,
+ *              16-byte aligned (per-workgroup partial maxima of the amax pass;
+ *              no initialisation needed).  Calls that may run concurrently
+ *              (different streams) need separate workspaces.
  * Enqueues two kernels (amax pass, quantise pass) on `stream`.
  * Writes codes, scales, *global_scale and *amax of every output.
  * RHT signs: d_j = -1 iff bit (j mod 16) of nvfp4_rht_sign_mask(rht_seed),
@@ -123,7 +125,8 @@ typedef struct {
 int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
                    int n_outs, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace nvfp4_quantize needs (a small constant). */
+/* Bytes of device workspace nvfp4_quantize needs (a small constant: partial
+ * maxima of up to 1024 workgroups per amax mode). */
 size_t nvfp4_workspace_bytes(void);
 
 /*

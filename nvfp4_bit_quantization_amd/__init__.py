@@ -151,6 +151,7 @@ def output_shape(rows: int, cols: int, layout: int):
 
 
 def new_workspace(device="cuda"):
+    """A quantise workspace (one per stream)."""
     import torch
     return torch.empty(lib().nvfp4_workspace_bytes() // 4, dtype=torch.float32, device=device)
 

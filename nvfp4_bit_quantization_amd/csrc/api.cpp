@@ -99,7 +99,7 @@ OutArgs out_args(const nvfp4_quant_output &o, int amax_mode) {
 
 extern "C" {
 
-size_t nvfp4_workspace_bytes(void) { return sizeof(float) * 3 * (size_t)kMaxParts; }
+size_t nvfp4_workspace_bytes(void) { return kWsBytes; }
 
 uint16_t nvfp4_rht_sign_mask(uint64_t rht_seed) {
   const uint32_t ctr[4] = {0u, 0u, 1u, 0u};
@@ -161,9 +161,28 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
 
   hipStream_t s = (hipStream_t)stream;
   const int tiles = quant_tiles(rows, cols);
-  const int nparts = tiles < kMaxParts ? tiles : kMaxParts;
   float *partials = (float *)workspace;
 
+  QuantArgs qa;
+  qa.x = (const uint16_t *)x;
+  qa.R = rows;
+  qa.C = cols;
+  qa.ld = ld_x;
+  qa.partials = partials;
+  qa.mask_rows = mask_rows;
+  qa.mask_cols = mask_cols;
+  const OutPlan &p0 = p[order[0]];
+  qa.o[0] = out_args(outs[order[0]], p0.amax_mode);
+  OutPlan p1 = {G_NONE, false, false, AM_PLAIN};
+  if (n_outs == 2) {
+    p1 = p[order[1]];
+    qa.o[1] = out_args(outs[order[1]], p1.amax_mode);
+  } else {
+    qa.o[1] = qa.o[0];
+  }
+  bool supported = true;
+
+  const int nparts = tiles < kMaxParts ? tiles : kMaxParts;
   AmaxArgs aa;
   aa.x = (const uint16_t *)x;
   aa.R = rows;
@@ -180,26 +199,7 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
   }
   hipError_t e = launch_amax(aa, plain, rc, rr, nparts, s);
   if (e != hipSuccess) return NVFP4_E_HIP;
-
-  QuantArgs qa;
-  qa.x = (const uint16_t *)x;
-  qa.R = rows;
-  qa.C = cols;
-  qa.ld = ld_x;
-  qa.partials = partials;
   qa.nparts = nparts;
-  qa.mask_rows = mask_rows;
-  qa.mask_cols = mask_cols;
-  const OutPlan &p0 = p[order[0]];
-  qa.o[0] = out_args(outs[order[0]], p0.amax_mode);
-  OutPlan p1 = {G_NONE, false, false, AM_PLAIN};
-  if (n_outs == 2) {
-    p1 = p[order[1]];
-    qa.o[1] = out_args(outs[order[1]], p1.amax_mode);
-  } else {
-    qa.o[1] = qa.o[0];
-  }
-  bool supported = true;
   e = launch_quantize(qa, p0.geom, p0.rht, p0.sr, p1.geom, p1.rht, p1.sr, s, &supported);
   if (!supported) return NVFP4_E_UNSUPPORTED;
   return finish(e, s);

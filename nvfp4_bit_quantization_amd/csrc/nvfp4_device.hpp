@@ -52,20 +52,19 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 
 // Stochastic rounding with a 16-bit uniform: a' = min(|y|, 6) lies between grid
 // neighbours lo <= a' <= hi; round up iff u16 < 65536 * (a' - lo) / (hi - lo).
-// For a' >= 1 the grid points are the binary32 values with one mantissa bit,
-// so lo is a' with the low 22 mantissa bits cleared and the fraction is those
-// bits / 2^22 (u16 < d / 64 <=> 64 u16 < d).  Below 1 the spacing is 1/2:
-// frac = 2a' - floor(2a'), every step exact.  Branch-free: both forms are
-// evaluated and the right one selected.
+// For a' >= 1 the grid points are the binary32 values with one mantissa bit:
+// a step is one unit of bit 22, and the low 22 bits d give the fraction d / 2^22,
+// so rounding up (d > 64 u16) is exactly a carry into bit 22 when 2^22 - 1 -
+// 64 u16 is added; the carry also crosses binades (1.5 -> 2, 3 -> 4).  Below 1
+// the spacing is 1/2: t = 2a' is exact and its fraction t - floor(t) is
+// compared in binary32 (exact).  Both forms are evaluated and one selected.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
   const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
   const float a = fminf(fabsf(y), 6.0f);
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t code_hi = (u >> 22) - 252u + (((u16 << 6) < (u & 0x3FFFFFu)) ? 1u : 0u);
+  const uint32_t code_hi = ((__float_as_uint(a) + (0x3FFFFFu - (u16 << 6))) >> 22) - 252u;
   const float t = a * 2.0f;
-  const float fl = __builtin_floorf(t);
-  const float fr = t - fl;
-  const uint32_t code_lo = (uint32_t)fl + (((float)u16 < fr * 65536.0f) ? 1u : 0u);
+  const float fr = __builtin_amdgcn_fractf(t);
+  const uint32_t code_lo = (uint32_t)t + (((float)u16 < fr * 65536.0f) ? 1u : 0u);
   return (a >= 1.0f ? code_hi : code_lo) | sign;
 }
 
@@ -105,16 +104,18 @@ __device__ __forceinline__ uint32_t u16_of(const uint32_t w[4], int k) {  // k =
 }
 
 // ------------------------------------------------------------ Hadamard ----
-// In-place 16-point fast Walsh-Hadamard transform in binary64 (Sylvester
-// order: out_i = sum_j (-1)^popcount(i&j) in_j).  With bf16 inputs every
-// partial sum is exact while the 16 inputs span fewer than 41 binades.
-__device__ __forceinline__ void fwht16(double v[16]) {
+// In-place 16-point fast Walsh-Hadamard transform in binary32 (Sylvester
+// order: out_i = sum_j (-1)^popcount(i&j) in_j).  Each butterfly addition is
+// rounded, so a result can differ from the exactly rounded sum by a few units
+// in the last place when the 16 inputs span many binades; the quantised
+// outputs of the RHT paths are compared with a tolerance for that reason.
+__device__ __forceinline__ void fwht16(float v[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & h) == 0) {
-        const double a = v[i], b = v[i + h];
+        const float a = v[i], b = v[i + h];
         v[i] = a + b;
         v[i + h] = a - b;
       }
@@ -127,27 +128,6 @@ __device__ __forceinline__ void fwht16(double v[16]) {
 __device__ __forceinline__ float swap8(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
 }
-__device__ __forceinline__ double swap8(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x128, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), 0x128, 0xF, 0xF, false);
-  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
-}
-
-// value of lane (lane ^ 1) / (lane ^ 2): DPP quad permutations
-__device__ __forceinline__ uint32_t xor1u(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); }
-__device__ __forceinline__ uint32_t xor2u(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ float xor1f(float v) { return __uint_as_float(xor1u(__float_as_uint(v))); }
-__device__ __forceinline__ float xor2f(float v) { return __uint_as_float(xor2u(__float_as_uint(v))); }
-__device__ __forceinline__ double xor1d(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  return __longlong_as_double((long long)(((uint64_t)xor1u((uint32_t)(u >> 32)) << 32) | xor1u((uint32_t)u)));
-}
-__device__ __forceinline__ double xor2d(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  return __longlong_as_double((long long)(((uint64_t)xor2u((uint32_t)(u >> 32)) << 32) | xor2u((uint32_t)u)));
-}
-
 // ------------------------------------------------------------- XCDs -------
 // Workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD works
 // on one contiguous range of tiles (neighbouring tiles share its L2).

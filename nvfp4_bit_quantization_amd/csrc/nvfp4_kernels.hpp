@@ -28,6 +28,9 @@ constexpr int kQTileC = 256;  // cols per quantise workgroup tile
 constexpr int kQThreads = 256;
 constexpr int kMaxParts = 1024;  // partial maxima per amax mode
 
+// Quantise workspace: partial maxima [3][kMaxParts] floats.
+constexpr size_t kWsBytes = sizeof(float) * 3 * kMaxParts;
+
 struct OutArgs {
   uint8_t *codes;
   uint8_t *scales;

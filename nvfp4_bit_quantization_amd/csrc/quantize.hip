@@ -1,412 +1,41 @@
-// NVFP4 quantisation kernels for gfx950: the per-tensor amax pass, the fused
-// (RHT +) block-scale + round + pack pass with one or two outputs from a single
-// read of the input, dequantisation, and the codec self-test kernel.
+// NVFP4 quantisation kernels for gfx950: the per-tensor amax pass and the
+// fused (RHT +) block-scale + round + pack pass with one or two outputs from a
+// single read of the input; dequantisation; the codec self-test kernel.  Their
+// device code is in quantize_device.hpp.
 //
-// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1
-// elements in 16-element blocks with an E4M3 scale per block and an FP32
-// per-tensor scale; 1D blocks for activations/gradients, 16x16 blocks for
-// weights; stochastic rounding for gradients; 16x16 random Hadamard transforms
-// with random signs on Wgrad inputs.
-//
-// Work decomposition.  A workgroup (4 waves) owns a 128 x 256 tile of the
-// bf16 input.  Each lane owns a 16-row x 8-column micro-tile, loaded as 16
-// 16-byte vectors; inside a wave the lanes form an 8 (column chunks) x 8
-// (row groups) grid, so one load instruction reads 128 contiguous bytes from
-// each of 8 rows.  A 16-element row block spans lanes l and l^8 (combined
-// with one DPP row rotate), a 16-element column block and the 16-point
-// Hadamard transform along rows live entirely inside one lane.
-#include "nvfp4_device.hpp"
-#include "nvfp4_kernels.hpp"
+// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2.
+#include "quantize_device.hpp"
 
 namespace nvfp4 {
 
-struct Lane {
-  int64_t r0, c0;  // top-left element of this lane's 16x8 micro-tile
-  uint32_t hi;     // 1 if the micro-tile is the right half of a 16-col block
-  bool valid;
-};
-
-__device__ __forceinline__ Lane lane_coords(uint32_t tile, int64_t R, int64_t C) {
-  const int64_t ntc = (C + kQTileC - 1) / kQTileC;
-  const int64_t tr = tile / ntc, tc = tile % ntc;
-  const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t cg = lane & 7, cc = lane >> 3;
-  Lane L;
-  L.r0 = tr * kQTileR + cg * 16;
-  L.c0 = tc * kQTileC + w * 64 + cc * 8;
-  L.hi = cc & 1;
-  L.valid = (L.r0 < R) && (L.c0 < C);
-  return L;
-}
-
-__device__ __forceinline__ void load_micro_tile(const uint16_t *x, int64_t ld, const Lane &L, uint4 raw[16]) {
-  const uint16_t *p = x + L.r0 * ld + L.c0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4 *>(p + i * ld);
-}
-
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  return m;
-}
-
-// ------------------------------------------------------------------------
-// RHT: sign vectors as XORs of the bf16 sign bits, then the butterflies
-// ------------------------------------------------------------------------
-// along rows: row i of the 16-row group gets d_i
-__device__ __forceinline__ void flip_rows(uint4 raw[16], uint32_t mask) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t f = ((mask >> i) & 1u) ? 0x80008000u : 0u;
-    raw[i].x ^= f;
-    raw[i].y ^= f;
-    raw[i].z ^= f;
-    raw[i].w ^= f;
-  }
-}
-// along columns: column j = 8 hi + k of the 16-column block gets d_j
-__device__ __forceinline__ void flip_cols(uint4 raw[16], uint32_t mask, uint32_t hi) {
-  const uint32_t m = mask >> (8 * hi);
-  uint32_t f[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) f[p] = (((m >> (2 * p)) & 1u) << 15) | (((m >> (2 * p + 1)) & 1u) << 31);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    raw[i].x ^= f[0];
-    raw[i].y ^= f[1];
-    raw[i].z ^= f[2];
-    raw[i].w ^= f[3];
-  }
-}
-
-// column j (16 rows, signs applied): H v in binary64 (the 1/4 is applied later)
-__device__ __forceinline__ void fwht_column(const uint4 raw[16], int j, double d[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) d[i] = (double)bf16_at(raw[i], j);
-  fwht16(d);
-}
-
-// row i of a 16-column block held by lanes l (cols 0..7) and l^8 (cols 8..15),
-// signs applied: butterflies on j bits 0-2 inside the lane, bit 3 across lanes
-__device__ __forceinline__ void fwht_row(const uint4 &row, uint32_t hi, double d[8]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) d[k] = (double)bf16_at(row, k);
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if ((k & h) == 0) {
-        const double a = d[k], b = d[k + h];
-        d[k] = a + b;
-        d[k + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const double other = swap8(d[k]);
-    d[k] = hi ? (other - d[k]) : (d[k] + other);
-  }
-}
-
-// ------------------------------------------------------------------------
-// amax pass: per-workgroup partial maxima for up to three modes
-// ------------------------------------------------------------------------
 template <bool PLAIN, bool RC, bool RR>
 __global__ __launch_bounds__(kQThreads) void amax_kernel(AmaxArgs a) {
   const int64_t ntiles = ((a.R + kQTileR - 1) / kQTileR) * ((a.C + kQTileC - 1) / kQTileC);
-  float m_plain = 0.0f;
-  double m_rc = 0.0, m_rr = 0.0;
+  float m_plain = 0.0f, m_rc = 0.0f, m_rr = 0.0f;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const Lane L = lane_coords((uint32_t)t, a.R, a.C);
     if (!L.valid) continue;  // pairs of lanes are valid together (C % 16 == 0)
     uint4 raw[16];
     load_micro_tile(a.x, a.ld, L, raw);
-    if (PLAIN) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) m_plain = fmaxf(m_plain, fabsf(bf16_at(raw[i], k)));
-    }
-    if (RC) {
-      uint4 r[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = raw[i];
-      flip_rows(r, a.mask_rows);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        double d[16];
-        fwht_column(r, j, d);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m_rc = fmax(m_rc, fabs(d[i]));
-      }
-    }
-    if (RR) {
-      uint4 r[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = raw[i];
-      flip_cols(r, a.mask_cols, L.hi);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        double d[8];
-        fwht_row(r[i], L.hi, d);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) m_rr = fmax(m_rr, fabs(d[k]));
-      }
-    }
+    tile_maxes<PLAIN, RC, RR>(raw, L, a.mask_rows, a.mask_cols, m_plain, m_rc, m_rr);
   }
-  // the quarter of the Hadamard normalisation is exact; rounding to binary32
-  // is monotonic, so the max of the rounded values is the rounded max
-  __shared__ float red[3][kQThreads / 64];
-  const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float v0 = wave_max(m_plain);
-  float v1 = wave_max((float)(m_rc * 0.25));
-  float v2 = wave_max((float)(m_rr * 0.25));
-  if (lane == 0) {
-    red[0][w] = v0;
-    red[1][w] = v1;
-    red[2][w] = v2;
-  }
-  __syncthreads();
-  if (threadIdx.x < 3) {
-    float m = red[threadIdx.x][0];
-    for (int i = 1; i < kQThreads / 64; ++i) m = fmaxf(m, red[threadIdx.x][i]);
-    const bool want = threadIdx.x == 0 ? PLAIN : threadIdx.x == 1 ? RC : RR;
-    if (want) a.partials[threadIdx.x * kMaxParts + blockIdx.x] = m;
-  }
+  write_partials<PLAIN, RC, RR>(m_plain, m_rc, m_rr, a.partials, blockIdx.x);
 }
 
-// ------------------------------------------------------------------------
-// element encoders over a lane's values
-// ------------------------------------------------------------------------
-// 8 values -> one 32-bit word of codes (value k in nibble k), RTN
-__device__ __forceinline__ uint32_t pack8_rtn(const float v[8], float rb) {
-  uint32_t w = NVFP4_CVT_PK_FP4(0u, v[0] * rb, v[1] * rb, 0);
-  w = NVFP4_CVT_PK_FP4(w, v[2] * rb, v[3] * rb, 1);
-  w = NVFP4_CVT_PK_FP4(w, v[4] * rb, v[5] * rb, 2);
-  w = NVFP4_CVT_PK_FP4(w, v[6] * rb, v[7] * rb, 3);
-  return w;
-}
-
-// 8 values -> word, SR with the uniforms of draw w[] (value k uses u16_of(w, k))
-__device__ __forceinline__ uint32_t pack8_sr(const float v[8], float rb, const uint32_t w[4]) {
-  uint32_t word = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) word |= e2m1_sr(v[k] * rb, u16_of(w, k)) << (4 * k);
-  return word;
-}
-
-__device__ __forceinline__ float block_scale(float bmax, float S, const float *lut, uint32_t *code) {
-  const float t = bmax / 6.0f;  // correctly rounded binary32 division
-  const float sb = t * S;
-  const uint32_t c = e4m3_encode(sb);
-  *code = c;
-  return lut[c];
-}
-
-// ------------------------------------------------------------------------
-// one output of the quantise pass
-// ------------------------------------------------------------------------
-template <int G, bool RHT, bool SR>
-__device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane &L, const OutArgs &o, float S,
-                                                const float *lut, int64_t R, int64_t C) {
-  if (G == G_ROW) {
-    const int64_t nbc = C / 16;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v[8];
-      if (RHT) {
-        double d[8];
-        fwht_row(raw[i], L.hi, d);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (float)(d[k] * 0.25);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = bf16_at(raw[i], k);
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-      m = fmaxf(m, swap8(m));
-      uint32_t sc;
-      const float rb = block_scale(m, S, lut, &sc);
-      const int64_t r = L.r0 + i;
-      const uint32_t blk = (uint32_t)(r * nbc + L.c0 / 16);
-      if (!L.hi) o.scales[blk] = (uint8_t)sc;
-      uint32_t word;
-      if (SR) {
-        uint32_t w[4];
-        sr_draw(o.sr_seed, blk, L.hi, w);
-        word = pack8_sr(v, rb, w);
-      } else {
-        word = pack8_rtn(v, rb);
-      }
-      *reinterpret_cast<uint32_t *>(o.codes + r * (C / 2) + L.c0 / 2) = word;
-    }
-  } else if (G == G_COL) {
-    const int64_t nbr = R / 16;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v[16];
-      if (RHT) {
-        double d[16];
-        fwht_column(raw, j, d);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = (float)(d[i] * 0.25);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = bf16_at(raw[i], j);
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-      uint32_t sc;
-      const float rb = block_scale(m, S, lut, &sc);
-      const int64_t c = L.c0 + j;
-      const uint32_t blk = (uint32_t)(c * nbr + L.r0 / 16);
-      o.scales[blk] = (uint8_t)sc;
-      uint2 words;
-      if (SR) {
-        uint32_t w[4];
-        sr_draw(o.sr_seed, blk, 0u, w);
-        words.x = pack8_sr(v, rb, w);
-        sr_draw(o.sr_seed, blk, 1u, w);
-        words.y = pack8_sr(v + 8, rb, w);
-      } else {
-        words.x = pack8_rtn(v, rb);
-        words.y = pack8_rtn(v + 8, rb);
-      }
-      *reinterpret_cast<uint2 *>(o.codes + c * (R / 2) + L.r0 / 2) = words;
-    }
-  } else {  // G_TILE or G_TILE_T: one scale per 16x16 tile (this lane and lane^8)
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(bf16_at(raw[i], k)));
-    m = fmaxf(m, swap8(m));
-    uint32_t sc;
-    const float rb = block_scale(m, S, lut, &sc);
-    const int64_t nbc = C / 16, nbr = R / 16;
-    if (G == G_TILE) {
-      if (!L.hi) o.scales[(L.r0 / 16) * nbc + L.c0 / 16] = (uint8_t)sc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = bf16_at(raw[i], k);
-        const int64_t r = L.r0 + i;
-        uint32_t word;
-        if (SR) {
-          uint32_t w[4];
-          sr_draw(o.sr_seed, (uint32_t)(r * nbc + L.c0 / 16), L.hi, w);
-          word = pack8_sr(v, rb, w);
-        } else {
-          word = pack8_rtn(v, rb);
-        }
-        *reinterpret_cast<uint32_t *>(o.codes + r * (C / 2) + L.c0 / 2) = word;
-      }
-    } else {
-      if (!L.hi) o.scales[(L.c0 / 16) * nbr + L.r0 / 16] = (uint8_t)sc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = bf16_at(raw[i], j);
-        uint2 words;
-        if (SR) {
-          // the uniforms follow the row-blocked numbering of the untransposed tensor
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            uint32_t w[4];
-            sr_draw(o.sr_seed, (uint32_t)((L.r0 + i) * nbc + L.c0 / 16), L.hi, w);
-            const uint32_t code = e2m1_sr(v[i] * rb, u16_of(w, j));
-            if (i < 8)
-              lo |= code << (4 * i);
-            else
-              hi |= code << (4 * (i - 8));
-          }
-          words.x = lo;
-          words.y = hi;
-        } else {
-          words.x = pack8_rtn(v, rb);
-          words.y = pack8_rtn(v + 8, rb);
-        }
-        *reinterpret_cast<uint2 *>(o.codes + (L.c0 + j) * (R / 2) + L.r0 / 2) = words;
-      }
-    }
-  }
-}
-
+// Quantise pass: one micro-tile per lane, global scales from the partial
+// maxima of the amax pass.
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantArgs a) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   __shared__ float s_lut[2][128];
-  __shared__ float s_red[kQThreads / 64];
   __shared__ float s_S[2];
-
   const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const Lane L = lane_coords(tile, a.R, a.C);
   uint4 raw[16];
   if (L.valid) load_micro_tile(a.x, a.ld, L, raw);
-
-  // global scale of each output from the partial maxima of the amax pass
-  const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 0; o < NOUT; ++o) {
-    const float *part = a.partials + a.o[o].amax_mode * kMaxParts;
-    float m = 0.0f;
-    for (int p = threadIdx.x; p < a.nparts; p += kQThreads) m = fmaxf(m, part[p]);
-    m = wave_max(m);
-    if (lane == 0) s_red[w] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float amax = s_red[0];
-      for (int i = 1; i < kQThreads / 64; ++i) amax = fmaxf(amax, s_red[i]);
-      float S = 2688.0f / amax;  // 448 * 6
-      if (amax == 0.0f || !__builtin_isfinite(S)) S = 1.0f;
-      s_S[o] = S;
-      if (blockIdx.x == 0) {
-        *a.o[o].S_out = S;
-        *a.o[o].amax_out = amax;
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < 127) {
-      const float S = s_S[o];
-      const float val = e4m3_value(threadIdx.x);
-      s_lut[o][threadIdx.x] = (val == 0.0f) ? 0.0f : S / val;
-    }
-  }
-  __syncthreads();
+  quant_setup<NOUT>(a, (uint32_t)a.nparts, s_S, s_lut);
   if (!L.valid) return;
-
-  // outputs without the RHT first, then the RHT ones with their sign vector
-  // XORed into the raw bf16 values
-  if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
-  if (NOUT == 2 && !RHT1) quantize_output<G1, false, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
-  if (RHT0) {
-    if (G0 == G_COL)
-      flip_rows(raw, a.mask_rows);
-    else
-      flip_cols(raw, a.mask_cols, L.hi);
-    quantize_output<G0, true, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
-    if (NOUT == 2 && RHT1) {  // undo
-      if (G0 == G_COL)
-        flip_rows(raw, a.mask_rows);
-      else
-        flip_cols(raw, a.mask_cols, L.hi);
-    }
-  }
-  if (NOUT == 2 && RHT1) {
-    if (G1 == G_COL)
-      flip_rows(raw, a.mask_rows);
-    else
-      flip_cols(raw, a.mask_cols, L.hi);
-    quantize_output<G1, true, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
-  }
+  quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut);
 }
 
 // ------------------------------------------------------------------------
@@ -482,59 +111,47 @@ hipError_t launch_amax(const AmaxArgs &a, bool plain, bool rc, bool rr, int npar
 }
 
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
-static void launch_q(const QuantArgs &a, hipStream_t s) {
-  const dim3 grid(quant_tiles(a.R, a.C)), block(kQThreads);
-  hipLaunchKernelGGL((quantize_kernel<G0, RHT0, SR0, G1, RHT1, SR1>), grid, block, 0, s, a);
+static hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((quantize_kernel<G0, RHT0, SR0, G1, RHT1, SR1>), dim3(quant_tiles(a.R, a.C)), dim3(kQThreads),
+                     0, s, a);
+  return hipGetLastError();
 }
 
-// single outputs
 template <int G, bool RHT>
-static bool dispatch_single(const QuantArgs &a, bool sr, hipStream_t s) {
-  if (sr)
-    launch_q<G, RHT, true, G_NONE, false, false>(a, s);
-  else
-    launch_q<G, RHT, false, G_NONE, false, false>(a, s);
-  return true;
+static hipError_t dispatch_single(const QuantArgs &a, bool sr, hipStream_t s) {
+  return sr ? launch_q<G, RHT, true, G_NONE, false, false>(a, s) : launch_q<G, RHT, false, G_NONE, false, false>(a, s);
 }
 
 // {ROW, COL} pairs: g0 = ROW, g1 = COL
 template <bool RHT0, bool RHT1>
-static void dispatch_row_col(const QuantArgs &a, bool sr0, bool sr1, hipStream_t s) {
-  if (!sr0 && !sr1) launch_q<G_ROW, RHT0, false, G_COL, RHT1, false>(a, s);
-  if (!sr0 && sr1) launch_q<G_ROW, RHT0, false, G_COL, RHT1, true>(a, s);
-  if (sr0 && !sr1) launch_q<G_ROW, RHT0, true, G_COL, RHT1, false>(a, s);
-  if (sr0 && sr1) launch_q<G_ROW, RHT0, true, G_COL, RHT1, true>(a, s);
+static hipError_t dispatch_row_col(const QuantArgs &a, bool sr0, bool sr1, hipStream_t s) {
+  if (!sr0 && !sr1) return launch_q<G_ROW, RHT0, false, G_COL, RHT1, false>(a, s);
+  if (!sr0 && sr1) return launch_q<G_ROW, RHT0, false, G_COL, RHT1, true>(a, s);
+  if (sr0 && !sr1) return launch_q<G_ROW, RHT0, true, G_COL, RHT1, false>(a, s);
+  return launch_q<G_ROW, RHT0, true, G_COL, RHT1, true>(a, s);
 }
 
 hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int g1, bool rht1, bool sr1,
                            hipStream_t s, bool *supported) {
   *supported = true;
   if (g1 == G_NONE) {
-    if (g0 == G_ROW)
-      rht0 ? dispatch_single<G_ROW, true>(a, sr0, s) : dispatch_single<G_ROW, false>(a, sr0, s);
-    else if (g0 == G_COL)
-      rht0 ? dispatch_single<G_COL, true>(a, sr0, s) : dispatch_single<G_COL, false>(a, sr0, s);
-    else if (g0 == G_TILE && !rht0)
-      dispatch_single<G_TILE, false>(a, sr0, s);
-    else if (g0 == G_TILE_T && !rht0)
-      dispatch_single<G_TILE_T, false>(a, sr0, s);
-    else
-      *supported = false;
+    if (g0 == G_ROW) return rht0 ? dispatch_single<G_ROW, true>(a, sr0, s) : dispatch_single<G_ROW, false>(a, sr0, s);
+    if (g0 == G_COL) return rht0 ? dispatch_single<G_COL, true>(a, sr0, s) : dispatch_single<G_COL, false>(a, sr0, s);
+    if (g0 == G_TILE && !rht0) return dispatch_single<G_TILE, false>(a, sr0, s);
+    if (g0 == G_TILE_T && !rht0) return dispatch_single<G_TILE_T, false>(a, sr0, s);
   } else if (g0 == G_ROW && g1 == G_COL) {
-    if (!rht0 && !rht1) dispatch_row_col<false, false>(a, sr0, sr1, s);
-    if (!rht0 && rht1) dispatch_row_col<false, true>(a, sr0, sr1, s);
-    if (rht0 && !rht1) dispatch_row_col<true, false>(a, sr0, sr1, s);
-    if (rht0 && rht1) dispatch_row_col<true, true>(a, sr0, sr1, s);
+    if (!rht0 && !rht1) return dispatch_row_col<false, false>(a, sr0, sr1, s);
+    if (!rht0 && rht1) return dispatch_row_col<false, true>(a, sr0, sr1, s);
+    if (rht0 && !rht1) return dispatch_row_col<true, false>(a, sr0, sr1, s);
+    return dispatch_row_col<true, true>(a, sr0, sr1, s);
   } else if (g0 == G_TILE && g1 == G_TILE_T && !rht0 && !rht1) {
-    if (!sr0 && !sr1) launch_q<G_TILE, false, false, G_TILE_T, false, false>(a, s);
-    if (!sr0 && sr1) launch_q<G_TILE, false, false, G_TILE_T, false, true>(a, s);
-    if (sr0 && !sr1) launch_q<G_TILE, false, true, G_TILE_T, false, false>(a, s);
-    if (sr0 && sr1) launch_q<G_TILE, false, true, G_TILE_T, false, true>(a, s);
-  } else {
-    *supported = false;
+    if (!sr0 && !sr1) return launch_q<G_TILE, false, false, G_TILE_T, false, false>(a, s);
+    if (!sr0 && sr1) return launch_q<G_TILE, false, false, G_TILE_T, false, true>(a, s);
+    if (sr0 && !sr1) return launch_q<G_TILE, false, true, G_TILE_T, false, false>(a, s);
+    return launch_q<G_TILE, false, true, G_TILE_T, false, true>(a, s);
   }
-  if (!*supported) return hipErrorInvalidValue;
-  return hipGetLastError();
+  *supported = false;
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {
@@ -553,5 +170,4 @@ hipError_t launch_codec_selftest(int which, const float *in, const uint16_t *u16
   hipLaunchKernelGGL(codec_selftest_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, which, in, u16, out, n);
   return hipGetLastError();
 }
-
 }  // namespace nvfp4
