@@ -354,14 +354,14 @@ def main():
     dms = t.ms(dom)
     if dc["kind"] == "gemm":
         achieved = dc["flops"] / (dms * 1e-3) / 1e12
-        src = source_hash("gemm.hip", "nvfp4_device.hpp")
+        src = source_hash("gemm.hip", "nvfp4_device.hpp", "nvfp4_kernels.hpp")
         traffic = read_traffic("gemm_" + args.workload, src)
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4), traffic=traffic, kernel="gemm_kernel<4,4>",
+                    frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4), traffic=traffic, kernel="gemm_fast_kernel<4,4>",
                     ms=round(dms, 4), source_hash=src)
     else:
         achieved = dc["bytes"] / (dms * 1e-3) / 1e9
-        src = source_hash("quantize.hip", "nvfp4_device.hpp")
+        src = source_hash("quantize.hip", "quantize_device.hpp", "nvfp4_device.hpp", "nvfp4_kernels.hpp")
         traffic = read_traffic("quantize_" + args.workload, src)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel="amax+quantize pass",

@@ -246,6 +246,7 @@ constexpr int kFBK = 128;
 constexpr int kFStageCodes = 512 * 64;         // bytes of codes per stage
 constexpr int kFStageBytes = kFStageCodes + 512 * 8;
 constexpr int kFStages = 3;
+constexpr uint32_t kGroupM = 4;  // tile rows per group of the tile order
 
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
 
@@ -339,10 +340,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   static_assert(TM == 4 && TN == 4, "fast path is laid out for 256x256 tiles");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFStages * kFStageBytes];
 
-  const int64_t tiles_n = g.N / 256;
+  // Each XCD takes a contiguous range of the tile sequence, and the sequence
+  // runs down groups of kGroupM tile rows column by column, so the workgroups
+  // that one XCD runs at a time cover a compact block of C: they share the A
+  // and B K-slices in that XCD's L2 instead of each streaming its own.
+  const uint32_t tiles_m = (uint32_t)(g.M / 256), tiles_n = (uint32_t)(g.N / 256);
   const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t m0 = (int64_t)(tile / tiles_n) * 256;
-  const int64_t n0 = (int64_t)(tile % tiles_n) * 256;
+  const uint32_t group = tile / (kGroupM * tiles_n), first_m = group * kGroupM;
+  const uint32_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const uint32_t local = tile - group * kGroupM * tiles_n;
+  const int64_t m0 = (int64_t)(first_m + local % gm) * 256;
+  const int64_t n0 = (int64_t)(local / gm) * 256;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lr = lane & 31, h = lane >> 5;
