@@ -100,7 +100,7 @@ def setup_wgrad(nv, syn, tokens=8192, hidden=5120):
     import torch
     dy_bits, x_bits = syn.wgrad_8192x5120(tokens, hidden)
     dy, x = dev_bf16(dy_bits), dev_bf16(x_bits)
-    ws = nv.new_workspace()
+    ws, gws = nv.new_workspace(), nv.new_gemm_workspace()
     s_dy = [nv.QuantSpec.of("col", "sr", True, 1234, 1234)]
     s_x = [nv.QuantSpec.of("col", "rtn", True, 0, 1234)]
     q_dy = [nv.empty_qtensor(hidden, tokens, nv.SCALE_1D16, rht=1)]
@@ -111,7 +111,7 @@ def setup_wgrad(nv, syn, tokens=8192, hidden=5120):
     def step(t: Timer):
         t.run("quantize_dY", lambda: nv.nvfp4_quantize(dy, s_dy, q_dy, ws))
         t.run("quantize_X", lambda: nv.nvfp4_quantize(x, s_x, q_x, ws))
-        t.run("gemm_wgrad", lambda: nv.nvfp4_gemm(q_dy[0], q_x[0], c))
+        t.run("gemm_wgrad", lambda: nv.nvfp4_gemm(q_dy[0], q_x[0], c, gws))
 
     info = dict(flops=flops, calls={
         "quantize_dY": dict(kind="quantize", bytes=qbytes(tokens, hidden)),
@@ -178,7 +178,7 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
     d = syn.linear_step_16384(tokens, hidden, ffn)
     X, W1, W2, dY = (dev_bf16(d[k]) for k in ("X", "W1", "W2", "dY"))
     del d
-    ws = nv.new_workspace()
+    ws, gws = nv.new_workspace(), nv.new_gemm_workspace()
     bf, f32 = torch.bfloat16, torch.float32
     H = torch.empty((tokens, ffn), dtype=bf, device="cuda")
     Y = torch.empty((tokens, hidden), dtype=bf, device="cuda")
@@ -203,16 +203,16 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
     def step(t):
         t.run("q_X", lambda: nv.nvfp4_quantize(X, sX, qX, ws))
         t.run("q_W1", lambda: nv.nvfp4_quantize(W1, sW, qW1, ws))
-        t.run("fprop_H", lambda: nv.nvfp4_gemm(qX[0], qW1[0], H))
+        t.run("fprop_H", lambda: nv.nvfp4_gemm(qX[0], qW1[0], H, gws))
         t.run("q_H", lambda: nv.nvfp4_quantize(H, sX, qH, ws))
         t.run("q_W2", lambda: nv.nvfp4_quantize(W2, sW, qW2, ws))
-        t.run("fprop_Y", lambda: nv.nvfp4_gemm(qH[0], qW2[0], Y))
+        t.run("fprop_Y", lambda: nv.nvfp4_gemm(qH[0], qW2[0], Y, gws))
         t.run("q_dY", lambda: nv.nvfp4_quantize(dY, sdY, qdY, ws))
-        t.run("dgrad_dH", lambda: nv.nvfp4_gemm(qdY[0], qW2[1], dH))
+        t.run("dgrad_dH", lambda: nv.nvfp4_gemm(qdY[0], qW2[1], dH, gws))
         t.run("q_dH", lambda: nv.nvfp4_quantize(dH, sdH, qdH, ws))
-        t.run("dgrad_dX", lambda: nv.nvfp4_gemm(qdH[0], qW1[1], dX))
-        t.run("wgrad_dW2", lambda: nv.nvfp4_gemm(qdY[1], qH[1], dW2))
-        t.run("wgrad_dW1", lambda: nv.nvfp4_gemm(qdH[1], qX[1], dW1))
+        t.run("dgrad_dX", lambda: nv.nvfp4_gemm(qdH[0], qW1[1], dX, gws))
+        t.run("wgrad_dW2", lambda: nv.nvfp4_gemm(qdY[1], qH[1], dW2, gws))
+        t.run("wgrad_dW1", lambda: nv.nvfp4_gemm(qdH[1], qX[1], dW1, gws))
 
     calls = {
         "q_X": dict(kind="quantize", bytes=qbytes(tokens, hidden, 2)),

@@ -145,10 +145,30 @@ int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream
  *   a : M x K quantised tensor (a->rows = M, a->cols = K)
  *   b : N x K quantised tensor (b->rows = N, b->cols = K); a->cols == b->cols
  *   c : device, [M][N] with row stride ldc elements, fp32 or bf16 (RNE)
- * Operands are expanded exactly to fp16 in LDS and multiplied on MFMA with
- * fp32 accumulation; the per-tensor scales are applied in the epilogue.
+ *   workspace : NULL, or device memory of at least nvfp4_gemm_workspace_bytes()
+ *              bytes, 16-byte aligned, ZERO-FILLED before its first use (every
+ *              call leaves its flag words at zero again).  With a workspace,
+ *              shapes with more than two rounds of 256x256 tiles whose last
+ *              round would leave more than a tenth of the compute units idle
+ *              run as stream-K: whole tiles for the full rounds, then the
+ *              remaining tiles' K-tiles spread evenly over one
+ *              persistent workgroup per compute unit (a cooperative launch),
+ *              the fp32 partial sums of a split tile added in the workspace.  Without one (or if the runtime
+ *              refuses the cooperative launch) every workgroup computes whole
+ *              tiles.  The environment variable NVFP4_GEMM_DATA_PARALLEL
+ *              forces whole tiles.  Calls that may run concurrently need
+ *              separate workspaces.  The stream-K wait is bounded: if it ever
+ *              times out, the word at byte offset 4096 of the workspace becomes
+ *              non-zero and that call's output is invalid.
+ * Operands are expanded exactly to fp16 in registers and multiplied on MFMA
+ * with fp32 accumulation; the per-tensor scales are applied in the epilogue.
  */
-int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *stream);
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Bytes of GEMM workspace for the current device (8 KiB of flags plus one
+ * 256 KiB fp32 tile per compute unit; 0 if no device is visible). */
+size_t nvfp4_gemm_workspace_bytes(void);
 
 /* Host: the 16-bit RHT sign mask for a seed (bit j set => d_j = -1):
  * the low 16 bits of word 0 of Philox4x32-10(key = seed, counter = (0,0,1,0)). */

@@ -69,7 +69,10 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_tensor), P, i64, P]
     L.nvfp4_gemm.restype = i32
-    L.nvfp4_gemm.argtypes = [ctypes.POINTER(nvfp4_tensor), ctypes.POINTER(nvfp4_tensor), P, ctypes.c_int32, i64, P]
+    L.nvfp4_gemm.argtypes = [ctypes.POINTER(nvfp4_tensor), ctypes.POINTER(nvfp4_tensor), P, ctypes.c_int32, i64, P,
+                             ctypes.c_size_t, P]
+    L.nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.nvfp4_gemm_workspace_bytes.argtypes = []
     L.nvfp4_rht_sign_mask.restype = ctypes.c_uint16
     L.nvfp4_rht_sign_mask.argtypes = [ctypes.c_uint64]
     L.nvfp4_status_string.restype = ctypes.c_char_p
@@ -185,17 +188,35 @@ def nvfp4_dequantize(q: QTensor, y, stream=None):
     return y
 
 
-def nvfp4_gemm(a: QTensor, b: QTensor, c, stream=None):
-    """C[M][N] = A^ B^T / (S_A S_B) into the fp32 or bf16 device tensor c."""
+def nvfp4_gemm(a: QTensor, b: QTensor, c, workspace=None, stream=None):
+    """C[M][N] = A^ B^T / (S_A S_B) into the fp32 or bf16 device tensor c.
+    `workspace` (from new_gemm_workspace) enables the stream-K path."""
     import torch
     dt = F32 if c.dtype == torch.float32 else BF16 if c.dtype == torch.bfloat16 else None
     if dt is None:
         raise TypeError("c must be float32 or bfloat16")
     assert c.stride(1) == 1
     ta, tb = a.c_struct(), b.c_struct()
+    wp = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().nvfp4_gemm(ctypes.byref(ta), ctypes.byref(tb), ctypes.c_void_p(c.data_ptr()), dt, c.stride(0),
-                            _stream(stream)), "nvfp4_gemm")
+                            wp, wb, _stream(stream)), "nvfp4_gemm")
     return c
+
+
+def nvfp4_gemm_workspace_bytes() -> int:
+    return lib().nvfp4_gemm_workspace_bytes()
+
+
+def new_gemm_workspace(device="cuda"):
+    """A zero-filled GEMM workspace (one per stream)."""
+    import torch
+    return torch.zeros(lib().nvfp4_gemm_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def gemm_workspace_timed_out(workspace) -> bool:
+    """True if a stream-K call on this workspace hit its wait limit."""
+    return bool(workspace[4096:4100].view(__import__("torch").int32).item() != 0)
 
 
 def nvfp4_workspace_bytes() -> int:
@@ -237,8 +258,8 @@ def dequantize(q: QTensor, stream=None):
     return nvfp4_dequantize(q, y, stream)
 
 
-def gemm(a: QTensor, b: QTensor, out_dtype="f32", stream=None):
+def gemm(a: QTensor, b: QTensor, out_dtype="f32", workspace=None, stream=None):
     import torch
     dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
     c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
-    return nvfp4_gemm(a, b, c, stream)
+    return nvfp4_gemm(a, b, c, workspace, stream)

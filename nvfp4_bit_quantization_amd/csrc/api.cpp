@@ -224,7 +224,16 @@ int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream
   return finish(launch_dequantize(a, s), s);
 }
 
-int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *stream) {
+size_t nvfp4_gemm_workspace_bytes(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    return 0;
+  return gemm_workspace_bytes(cus < kGemmMaxCUs ? cus : kGemmMaxCUs);
+}
+
+int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *workspace,
+               size_t workspace_bytes, void *stream) {
   if (!a || !b || !c) return NVFP4_E_NULL;
   if (!a->codes || !a->scales || !a->global_scale || !b->codes || !b->scales || !b->global_scale) return NVFP4_E_NULL;
   if (a->rows <= 0 || b->rows <= 0 || a->cols <= 0 || (a->rows % 16) || (b->rows % 16) || (a->cols % 16))
@@ -236,6 +245,7 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_
     return NVFP4_E_UNSUPPORTED;
   if (ldc < b->rows) return NVFP4_E_LD;
   if (!aligned16(a->codes) || !aligned16(b->codes) || !aligned16(c)) return NVFP4_E_ALIGN;
+  if (workspace && !aligned16(workspace)) return NVFP4_E_ALIGN;
   if (a->rows > ((int64_t)1 << 31) || b->rows > ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
   GemmArgs g;
   g.a_codes = a->codes;
@@ -253,7 +263,7 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_
   g.b_kind = b->scale_kind;
   g.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
-  return finish(launch_gemm(g, s), s);
+  return finish(launch_gemm(g, workspace, workspace_bytes, s), s);
 }
 
 int nvfp4_codec_selftest(int which, const float *in_f32, const uint16_t *in_u16, uint8_t *out_u8, int64_t n,

@@ -335,22 +335,23 @@ __device__ __forceinline__ void interleave_step() {
   }
 }
 
-template <int TM, int TN>
-__global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
-  static_assert(TM == 4 && TN == 4, "fast path is laid out for 256x256 tiles");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kFStages * kFStageBytes];
-
-  // Each XCD takes a contiguous range of the tile sequence, and the sequence
-  // runs down groups of kGroupM tile rows column by column, so the workgroups
-  // that one XCD runs at a time cover a compact block of C: they share the A
-  // and B K-slices in that XCD's L2 instead of each streaming its own.
+// origin of tile t of the grouped order (see gemm_fast_kernel)
+__device__ __forceinline__ void tile_origin(const GemmArgs &g, uint32_t tile, int64_t &m0, int64_t &n0) {
   const uint32_t tiles_m = (uint32_t)(g.M / 256), tiles_n = (uint32_t)(g.N / 256);
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const uint32_t group = tile / (kGroupM * tiles_n), first_m = group * kGroupM;
   const uint32_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
   const uint32_t local = tile - group * kGroupM * tiles_n;
-  const int64_t m0 = (int64_t)(first_m + local % gm) * 256;
-  const int64_t n0 = (int64_t)(local / gm) * 256;
+  m0 = (int64_t)(first_m + local % gm) * 256;
+  n0 = (int64_t)(local / gm) * 256;
+}
+
+// Accumulate K-tiles [ka, kb) of the 256x256 C tile at (m0, n0) into acc.
+// Every wave of the workgroup calls it with the same arguments; it owns the
+// whole LDS pipeline while it runs (it starts with a barrier, so the stages
+// may be reused from one call to the next, and ends with no transfer in
+// flight).
+__device__ __forceinline__ void fast_tile(const GemmArgs &g, int64_t m0, int64_t n0, uint32_t ka, uint32_t kb,
+                                          float16v acc[4][4], uint8_t *lds) {
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lr = lane & 31, h = lane >> 5;
@@ -379,26 +380,18 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     c.soff[i] = srow * kblocks + half * 4u;
   }
 
-  float16v acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   // LDS byte offsets (within a stage) of this lane's fragments: [i][0] holds
   // the k of the first half of the K-tile (sub-steps 0-3), [i][1] the second
-  uint32_t aoff[TM][2], boff[TN][2], asoff[TM], bsoff[TN];
+  uint32_t aoff[4][2], boff[4][2], asoff[4], bsoff[4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const uint32_t r = wm * 128 + i * 32 + lr;
     aoff[i][0] = (r * 4 + ((2 * h) ^ swz(r))) * 16;
     aoff[i][1] = (r * 4 + ((2 * h + 1) ^ swz(r))) * 16;
     asoff[i] = kFStageCodes + (r * 2 + (h ^ ((r >> 4) & 1u))) * 4;
   }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const uint32_t r = 256 + wn * 128 + j * 32 + lr;
     boff[j][0] = (r * 4 + ((2 * h) ^ swz(r))) * 16;
     boff[j][1] = (r * 4 + ((2 * h + 1) ^ swz(r))) * 16;
@@ -414,27 +407,30 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   // kt+1 sits between the two halves of tile kt, and the fp16 fragments are
   // expanded one MFMA sub-step ahead, so MFMAs are ready on both sides of it.
   const uint32_t lds0 = lds_addr(lds);
-  const uint32_t KT = (uint32_t)(g.K / kFBK), klast = KT - 1;
-  fast_issue<0, 12>(c, lds0, 0, wave);
-  fast_issue<0, 12>(c, lds0 + kFStageBytes, klast < 1 ? klast : 1, wave);
-  fast_issue<0, 6>(c, lds0 + 2 * kFStageBytes, klast < 2 ? klast : 2, wave);
-  NVFP4_WAIT_VMCNT(18);  // this wave's transfers of tile 0 are done
+  const uint32_t klast = kb - 1;
+  NVFP4_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();  // no wave still reads the stages (a previous tile's)
+  asm volatile("" ::: "memory");
+  fast_issue<0, 12>(c, lds0, ka, wave);
+  fast_issue<0, 12>(c, lds0 + kFStageBytes, ka + 1 < klast ? ka + 1 : klast, wave);
+  fast_issue<0, 6>(c, lds0 + 2 * kFStageBytes, ka + 2 < klast ? ka + 2 : klast, wave);
+  NVFP4_WAIT_VMCNT(18);  // this wave's transfers of tile ka are done
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
   // first-half codes and the tile's scales (E4M3 -> fp16 pairs: lo = blocks
   // (4h, 4h+1) of the first half, hi = (4h+2, 4h+3) of the second)
-  uint4 qlo_a[TM], qlo_b[TN];
-  half2v sal[TM], sah[TM], sbl[TN], sbh[TN];
+  uint4 qlo_a[4], qlo_b[4];
+  half2v sal[4], sah[4], sbl[4], sbh[4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < 4; ++i) {
     qlo_a[i] = *reinterpret_cast<const uint4 *>(lds + aoff[i][0]);
     const uint32_t sw = *reinterpret_cast<const uint32_t *>(lds + asoff[i]);
     sal[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
     sah[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
   }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
+  for (int j = 0; j < 4; ++j) {
     qlo_b[j] = *reinterpret_cast<const uint4 *>(lds + boff[j][0]);
     const uint32_t sw = *reinterpret_cast<const uint32_t *>(lds + bsoff[j]);
     sbl[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
@@ -444,17 +440,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   expand_step<0>(f, qlo_a, qlo_b, sal, sbl);
 
   uint32_t stage = 0;
-  for (uint32_t kt = 0; kt < KT; ++kt) {
+  for (uint32_t kt = ka; kt < kb; ++kt) {
     // Each sub-step is a scheduling region of its own (sched_barrier), in
     // which the MFMAs of one sub-step interleave with the expansion of the next.
     const uint8_t *base = lds + stage * kFStageBytes;
     const uint32_t pstage = stage == 0 ? 2 : stage - 1;  // (kt + 2) % 3
     const uint32_t plds = lds0 + pstage * kFStageBytes, ptile = kt + 2 < klast ? kt + 2 : klast;
-    uint4 qhi_a[TM], qhi_b[TN];
+    uint4 qhi_a[4], qhi_b[4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) qhi_a[i] = *reinterpret_cast<const uint4 *>(base + aoff[i][1]);
+    for (int i = 0; i < 4; ++i) qhi_a[i] = *reinterpret_cast<const uint4 *>(base + aoff[i][1]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) qhi_b[j] = *reinterpret_cast<const uint4 *>(base + boff[j][1]);
+    for (int j = 0; j < 4; ++j) qhi_b[j] = *reinterpret_cast<const uint4 *>(base + boff[j][1]);
 
     // first half: sub-steps 0-3 (sub-step 0's fragments are ready)
     expand_step<1>(fn, qlo_a, qlo_b, sal, sbl);
@@ -478,11 +474,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     interleave_step();
     __builtin_amdgcn_sched_barrier(0);
 
-    half2v cah[TM], cbh[TN];
+    half2v cah[4], cbh[4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) cah[i] = sah[i];
+    for (int i = 0; i < 4; ++i) cah[i] = sah[i];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) cbh[j] = sbh[j];
+    for (int j = 0; j < 4; ++j) cbh[j] = sbh[j];
 
     NVFP4_WAIT_LGKM0();    // this wave's reads of the stage are complete
     NVFP4_WAIT_VMCNT(12);  // this wave's transfers of tile kt+1 are done (kt+2's may be in flight)
@@ -491,14 +487,14 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     const uint32_t dlds = lds_addr(base), dtile = kt + 3 < klast ? kt + 3 : klast;
     const uint32_t nstage = stage == 2 ? 0 : stage + 1;
     const uint8_t *nbase = lds + nstage * kFStageBytes;
-    uint32_t swa[TM], swb[TN];
+    uint32_t swa[4], swb[4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < 4; ++i) {
       qlo_a[i] = *reinterpret_cast<const uint4 *>(nbase + aoff[i][0]);
       swa[i] = *reinterpret_cast<const uint32_t *>(nbase + asoff[i]);
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < 4; ++j) {
       qlo_b[j] = *reinterpret_cast<const uint4 *>(nbase + boff[j][0]);
       swb[j] = *reinterpret_cast<const uint32_t *>(nbase + bsoff[j]);
     }
@@ -522,12 +518,12 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
     fast_issue<4, 2>(c, dlds, dtile, wave);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < 4; ++i) {
       sal[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i], 1.0f, false);
       sah[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swa[i], 1.0f, true);
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < 4; ++j) {
       sbl[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j], 1.0f, false);
       sbh[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(swb[j], 1.0f, true);
     }
@@ -538,15 +534,23 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   }
   NVFP4_WAIT_VMCNT(0);  // the clamped transfers of the last iterations
 
-  // epilogue: C = acc / (S_A S_B), 32-bit offsets from the tile origin
+}
+
+// C tile = acc / (S_A S_B), 32-bit offsets from the tile origin
+__device__ __forceinline__ void fast_store_c(const GemmArgs &g, int64_t m0, int64_t n0, const float16v acc[4][4]) {
+  const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lr = lane & 31, h = lane >> 5;
   const float inv = 1.0f / (*g.a_S * *g.b_S);
-  const uint32_t ldc = (uint32_t)g.ldc;
+  uint32_t ldc = (uint32_t)g.ldc;
+  asm volatile("" : "+s"(ldc));  // per-element offsets are formed here, not hoisted and kept live
   if (g.c_bf16) {
     uint16_t *ct = reinterpret_cast<uint16_t *>(g.c) + m0 * g.ldc + n0;
+    asm volatile("" : "+s"(ct));  // keep the address arithmetic in the epilogue
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
@@ -556,10 +560,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
         }
   } else {
     float *ct = reinterpret_cast<float *>(g.c) + m0 * g.ldc + n0;
+    asm volatile("" : "+s"(ct));  // keep the address arithmetic in the epilogue
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
@@ -569,19 +574,195 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   }
 }
 
+template <int TM, int TN>
+__global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
+  static_assert(TM == 4 && TN == 4, "fast path is laid out for 256x256 tiles");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFStages * kFStageBytes];
+  // Each XCD takes a contiguous range of the tile sequence, and the sequence
+  // runs down groups of kGroupM tile rows column by column, so the workgroups
+  // that one XCD runs at a time cover a compact block of C: they share the A
+  // and B K-slices in that XCD's L2 instead of each streaming its own.
+  int64_t m0, n0;
+  tile_origin(g, xcd_tile(blockIdx.x, gridDim.x), m0, n0);
+  float16v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  fast_tile(g, m0, n0, 0, (uint32_t)(g.K / kFBK), acc, lds);
+  fast_store_c(g, m0, n0, acc);
+}
+
+// ===========================================================================
+// Stream-K (fast path shapes whose tile count leaves compute units idle in
+// the last round): one persistent workgroup per compute unit, all resident
+// (a cooperative launch).  The first dp_tiles tiles (whole rounds) are done
+// as whole tiles, round by round, so that the workgroups of one XCD start
+// their tiles together and share K-slices in L2.  The remaining tiles' units
+// (tile, K-tile) are numbered tile by tile in the grouped order and dealt out
+// as G contiguous ranges.  A workgroup whose range starts inside a tile
+// computes that part first, writes its fp32 partial to workspace slot w and
+// raises flag w.  The workgroup that holds the tile's first K-tile (the head,
+// at the end of its range) computes its part last, then for each following
+// workgroup whose range starts inside the tile waits for its flag (normally
+// long raised), adds its partial (in workgroup order, so the sum does not
+// depend on timing) and lowers the flag, leaving every flag zero for the next
+// launch; then it writes C.  Partials and flags use device-coherent (sc1)
+// accesses; a partial's writes complete (vmcnt) before its flag is raised.
+// Each wait is bounded (about a second); on time-out `err` is set and that
+// tile's result is invalid, but the launch always ends.
+// ===========================================================================
+struct StreamK {
+  uint32_t *flags;  // [G]
+  uint32_t *err;
+  float *slots;     // [G][65536]
+  uint32_t tiles, KT;
+  uint32_t dp_tiles;  // tiles done whole before the stream-K part (a multiple of G)
+};
+
+// The partial moves 64 values at a time (a compiler memory barrier between
+// groups): four round trips to memory for the loads, and no more than 64
+// extra registers live next to the 256 accumulators.
+__device__ __forceinline__ void store_partial(float *slot, const float16v acc[4][4]) {
+  asm volatile("" : "+s"(slot));  // keep the address arithmetic here (not hoisted and kept live)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __hip_atomic_store(slot + ((i * 4 + j) * 16 + r) * kGThreads + threadIdx.x, acc[i][j][r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+  }
+}
+
+__device__ __forceinline__ void add_partial(float16v acc[4][4], const float *slot) {
+  asm volatile("" : "+s"(slot));  // keep the address arithmetic here (not hoisted and kept live)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p[4][16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p[j][r] = __hip_atomic_load(slot + ((i * 4 + j) * 16 + r) * kGThreads + threadIdx.x, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] += p[j][r];
+  }
+}
+
+__device__ __forceinline__ void zero_acc(float16v acc[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+__global__ __launch_bounds__(kGThreads) void gemm_streamk_kernel(GemmArgs g, StreamK sk) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFStages * kFStageBytes];
+  const uint32_t G = gridDim.x, w = xcd_tile(blockIdx.x, G);
+  float16v acc[4][4];
+  int64_t m0, n0;
+
+  for (uint32_t t = w; t < sk.dp_tiles; t += G) {  // whole tiles, round by round
+    tile_origin(g, t, m0, n0);
+    zero_acc(acc);
+    fast_tile(g, m0, n0, 0, sk.KT, acc, lds);
+    fast_store_c(g, m0, n0, acc);
+  }
+
+  const uint64_t U = (uint64_t)(sk.tiles - sk.dp_tiles) * sk.KT;
+  uint64_t u = U * w / G;
+  const uint64_t uend = U * (w + 1) / G;
+  while (u < uend) {
+    const uint32_t ts = (uint32_t)(u / sk.KT), ka = (uint32_t)(u - (uint64_t)ts * sk.KT);
+    const uint64_t tend = (uint64_t)(ts + 1) * sk.KT;
+    const uint32_t kb = (uint32_t)((uend < tend ? uend : tend) - (uint64_t)ts * sk.KT);
+    tile_origin(g, sk.dp_tiles + ts, m0, n0);
+    zero_acc(acc);
+    fast_tile(g, m0, n0, ka, kb, acc, lds);
+    if (ka > 0) {  // this range starts inside the tile: hand the partial to its head
+      store_partial(sk.slots + (size_t)w * 65536, acc);
+      NVFP4_WAIT_VMCNT(0);
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // head: add the partials of the following workgroups whose (non-empty)
+      // ranges start inside the tile
+      for (uint32_t v = w + 1; v < G && U * v / G < tend; ++v) {
+        if (U * (v + 1) / G == U * v / G) continue;  // an empty range wrote no partial
+        if (threadIdx.x == 0) {
+          for (uint32_t spins = 0;
+               __hip_atomic_load(sk.flags + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;) {
+            __builtin_amdgcn_s_sleep(8);
+            if (++spins == (1u << 22)) {
+              __hip_atomic_store(sk.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+        }
+        __syncthreads();
+        add_partial(acc, sk.slots + (size_t)v * 65536);
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(sk.flags + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      fast_store_c(g, m0, n0, acc);
+    }
+    u += kb - ka;
+  }
+}
+
 bool gemm_fast_ok(const GemmArgs &g) {
   return g.M % 256 == 0 && g.N % 256 == 0 && g.K % kFBK == 0 && g.K / 2 * (g.M > g.N ? g.M : g.N) < (1ll << 32) &&
          g.ldc * 256 < (1ll << 31);
 }
 
-hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
+size_t gemm_workspace_bytes(int cus) { return kGemmWsSlots + (size_t)cus * kGemmSlotBytes; }
+
+hipError_t launch_gemm(const GemmArgs &g, void *workspace, size_t workspace_bytes, hipStream_t s) {
   constexpr int TM = 4, TN = 4;
   constexpr int BM = GemmTile<TM, TN>::BM, BN = GemmTile<TM, TN>::BN;
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (gemm_fast_ok(g) && !getenv("NVFP4_GEMM_GENERIC"))
-    hipLaunchKernelGGL((gemm_fast_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);
-  else
+  if (!gemm_fast_ok(g) || getenv("NVFP4_GEMM_GENERIC")) {
     hipLaunchKernelGGL((gemm_generic_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);
+    return hipGetLastError();
+  }
+  // Stream-K when a workspace is given, there are more than two rounds of
+  // tiles and the last round would leave more than a tenth of the compute
+  // units idle.  (With fewer rounds the split tiles' pipeline refills and
+  // partial sums cost more than the idle units of one short last round, which
+  // also runs at a higher clock: measured on 5120x5120x8192.)
+  int dev = 0, cus = 0;
+  if (workspace && !getenv("NVFP4_GEMM_DATA_PARALLEL") && hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 &&
+      cus <= kGemmMaxCUs && tiles > 2 * (int64_t)cus && workspace_bytes >= gemm_workspace_bytes(cus)) {
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    if (10 * tiles < 9 * rounds * cus) {
+      StreamK sk;
+      sk.flags = (uint32_t *)workspace;
+      sk.err = (uint32_t *)workspace + kGemmMaxCUs;
+      sk.slots = (float *)((char *)workspace + kGemmWsSlots);
+      sk.tiles = (uint32_t)tiles;
+      sk.KT = (uint32_t)(g.K / kFBK);
+      sk.dp_tiles = (uint32_t)((tiles / cus) * cus);  // whole rounds first
+      GemmArgs ga = g;
+      void *params[] = {&ga, &sk};
+      const hipError_t e = hipLaunchCooperativeKernel((const void *)gemm_streamk_kernel, dim3((uint32_t)cus),
+                                                      dim3(kGThreads), params, 0, s);
+      if (e == hipSuccess) return e;
+      (void)hipGetLastError();  // refused: fall back to whole tiles
+    }
+  }
+  hipLaunchKernelGGL((gemm_fast_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);
   return hipGetLastError();
 }
 

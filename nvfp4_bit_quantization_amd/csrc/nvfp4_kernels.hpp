@@ -87,7 +87,13 @@ hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int 
                            hipStream_t s, bool *supported);
 int quant_tiles(int64_t R, int64_t C);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// GEMM workspace (stream-K path): kGemmMaxCUs flag words, an error word, then
+// from byte kGemmWsSlots one fp32 256x256 partial per compute unit.
+constexpr int kGemmMaxCUs = 1024;
+constexpr size_t kGemmWsSlots = 8192;
+constexpr size_t kGemmSlotBytes = 256 * 256 * 4;
+size_t gemm_workspace_bytes(int cus);
+hipError_t launch_gemm(const GemmArgs &a, void *workspace, size_t workspace_bytes, hipStream_t s);
 hipError_t launch_codec_selftest(int which, const float *in, const uint16_t *u16, uint8_t *out, int64_t n,
                                  hipStream_t s);
 

@@ -108,11 +108,14 @@ def test_dequantize_and_gemm_validation(L):
     b = _tensor(48, 32, nv.SCALE_2D16)
     bk = _tensor(48, 48, nv.SCALE_1D16)
     c = ctypes.c_void_p(FAKE)
-    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(bk), c, 0, 48, None) == -5   # K mismatch
-    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 3, 48, None) == -5    # dtype
-    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 40, None) == -3    # ldc < N
-    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), None, 0, 48, None) == -1
-    assert L.nvfp4_gemm(ctypes.byref(_tensor(64, 40, 0)), ctypes.byref(_tensor(48, 40, 0)), c, 0, 48, None) == -2
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(bk), c, 0, 48, None, 0, None) == -5   # K mismatch
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 3, 48, None, 0, None) == -5    # dtype
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 40, None, 0, None) == -3    # ldc < N
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), None, 0, 48, None, 0, None) == -1
+    assert L.nvfp4_gemm(ctypes.byref(_tensor(64, 40, 0)), ctypes.byref(_tensor(48, 40, 0)), c, 0, 48, None, 0,
+                        None) == -2
+    ws = ctypes.c_void_p(FAKE + 8)                                                         # misaligned workspace
+    assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 48, ws, 1 << 20, None) == -4
     assert L.nvfp4_codec_selftest(3, None, None, None, 0, None) == -5
     assert L.nvfp4_codec_selftest(0, None, None, None, -1, None) == -2
     assert L.nvfp4_codec_selftest(0, None, None, None, 5, None) == -1

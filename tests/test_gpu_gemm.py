@@ -97,14 +97,15 @@ def test_gemm_ldc_and_zero_operand(nv):
 
 def test_wgrad_8192x5120_sampled(nv):
     """dW = dY^T X: A = column-quantised dY (RHT + SR), B = column-quantised X
-    (RHT + RTN), both 5120 x 8192 stored; C fp32 5120x5120.  256 sampled rows
-    of C against the oracle on the GPU's own operands."""
+    (RHT + RTN), both 5120 x 8192 stored; C fp32 5120x5120 (with a workspace:
+    the stream-K launch the benchmark times).  256 sampled rows of C against
+    the oracle on the GPU's own operands."""
     dy, xx = syn.wgrad_8192x5120()
     say("wgrad quantize")
     qa = quant(nv, dy, "col", "sr", True, 1234, 1234)
     qb = quant(nv, xx, "col", "rtn", True, 0, 1234)
     say("wgrad gemm")
-    c = nv.gemm(qa, qb, "f32")
+    c = nv.gemm(qa, qb, "f32", workspace=nv.new_gemm_workspace())
     torch.cuda.synchronize()
     ga, gb = gpu_q_as_dict(qa), gpu_q_as_dict(qb)
     rows = np.sort(np.random.default_rng(7).choice(5120, size=256, replace=False))
@@ -117,3 +118,61 @@ def test_wgrad_8192x5120_sampled(nv):
     say("wgrad operand parity")
     assert_rht_tolerance(ga, oracle.quantize(dy, "col", "sr", True, 1234, 1234), "dY")
     assert_rht_tolerance(gb, oracle.quantize(xx, "col", "rtn", True, 0, 1234), "X")
+
+
+# ------------------------------------------------------------------ stream-K
+@pytest.fixture(scope="module")
+def gws(nv):
+    return nv.new_gemm_workspace()
+
+
+def _random_operands(M, N, K, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    def q(rows):
+        codes = torch.randint(0, 256, (rows, K // 2), dtype=torch.uint8, generator=g).cuda()
+        scales = torch.randint(0x20, 0x50, (rows, K // 16), dtype=torch.uint8, generator=g).cuda()
+        S = torch.tensor([0.75], dtype=torch.float32, device="cuda")
+        amax = torch.tensor([1.0], dtype=torch.float32, device="cuda")
+        return codes, scales, S, amax
+    import nvfp4_bit_quantization_amd as nvm
+    a, b = q(M), q(N)
+    qa = nvm.QTensor(a[0], a[1], a[2], a[3], M, K, nvm.SCALE_1D16)
+    qb = nvm.QTensor(b[0], b[1], b[2], b[3], N, K, nvm.SCALE_1D16)
+    return qa, qb
+
+
+@pytest.mark.parametrize("shape", [(4352, 8448, 1024), (5376, 6400, 512), (8192, 5120, 2048), (5376, 6400, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_streamk_matches_whole_tiles(nv, gws, shape, monkeypatch):
+    """More than two rounds of tiles with an ill-filled last round (561, 525
+    and 640 tiles on 256 compute units) take the stream-K path when a
+    workspace is given: whole tiles for the full rounds, then the remaining
+    K-tiles spread over every workgroup, split tiles' partial sums added in
+    the workspace (up to several parts per tile, and workgroups with empty
+    ranges when the remainder has fewer K-tiles than there are workgroups).
+    The result equals the whole-tile path's up to fp32 reassociation, is the
+    same bit for bit on every run, matches the oracle on sampled rows, and
+    leaves the workspace's flag and error words at zero.  K = 128 (one K-tile)
+    splits no tile."""
+    M, N, K = shape
+    qa, qb = _random_operands(M, N, K, seed=M + N + K)
+    say("stream-K", shape)
+    monkeypatch.delenv("NVFP4_GEMM_DATA_PARALLEL", raising=False)
+    c1 = nv.gemm(qa, qb, "f32", workspace=gws)
+    c2 = nv.gemm(qa, qb, "f32", workspace=gws)
+    monkeypatch.setenv("NVFP4_GEMM_DATA_PARALLEL", "1")
+    cd = nv.gemm(qa, qb, "f32", workspace=gws)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+    rel = (torch.linalg.norm((c1 - cd).double()) / torch.linalg.norm(cd.double())).item()
+    say("stream-K vs whole tiles rel", rel)
+    assert rel < 1e-6
+    words = host(gws[:4100].view(torch.int32))
+    assert not words.any() and not nv.gemm_workspace_timed_out(gws)
+    if K <= 1024:
+        ga, gb = gpu_q_as_dict(qa), gpu_q_as_dict(qb)
+        rows = np.sort(np.random.default_rng(M).choice(M, size=48, replace=False))
+        ref = oracle.round_output(oracle.gemm_f64(ga, gb, rows_a=rows), "f32")
+        err = rel_frobenius(host(c1)[rows], ref)
+        say("stream-K vs oracle", err)
+        assert err <= 1e-3

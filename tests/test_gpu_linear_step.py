@@ -74,19 +74,20 @@ def run_step(nv, T):
     odH = [("row", "sr", False, 1236, 0), ("col", "sr", True, 1237, 4321)]
 
     say("forward")
+    gws = nv.new_gemm_workspace()
     qX = nv.quantize(dev["X"], sX)
     qW1 = nv.quantize(dev["W1"], sW)
-    H = nv.gemm(qX[0], qW1[0], "bf16")             # H = X W1^T   [T][FFN]
+    H = nv.gemm(qX[0], qW1[0], "bf16", workspace=gws)             # H = X W1^T   [T][FFN]
     qH = nv.quantize(H, sX)
     qW2 = nv.quantize(dev["W2"], sW)
-    Y = nv.gemm(qH[0], qW2[0], "bf16")             # Y = H W2^T   [T][HID]
+    Y = nv.gemm(qH[0], qW2[0], "bf16", workspace=gws)             # Y = H W2^T   [T][HID]
     say("backward")
     qdY = nv.quantize(dev["dY"], sdY)
-    dH = nv.gemm(qdY[0], qW2[1], "bf16")           # dH = dY W2   [T][FFN]
+    dH = nv.gemm(qdY[0], qW2[1], "bf16", workspace=gws)           # dH = dY W2   [T][FFN]
     qdH = nv.quantize(dH, sdH)
-    dX = nv.gemm(qdH[0], qW1[1], "bf16")           # dX = dH W1   [T][HID]
-    dW2 = nv.gemm(qdY[1], qH[1], "f32")            # dW2 = dY^T H [HID][FFN]
-    dW1 = nv.gemm(qdH[1], qX[1], "f32")            # dW1 = dH^T X [FFN][HID]
+    dX = nv.gemm(qdH[0], qW1[1], "bf16", workspace=gws)           # dX = dH W1   [T][HID]
+    dW2 = nv.gemm(qdY[1], qH[1], "f32", workspace=gws)            # dW2 = dY^T H [HID][FFN]
+    dW1 = nv.gemm(qdH[1], qX[1], "f32", workspace=gws)            # dW1 = dH^T X [FFN][HID]
     torch.cuda.synchronize()
 
     say("quantisation parity")
