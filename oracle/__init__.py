@@ -111,6 +111,12 @@ def e2m1_value(code: int) -> float:
     return _load().oracle_e2m1_value(code)
 
 
+def e4m3_value_array(codes) -> np.ndarray:
+    """E4M3 decode of an array of codes (the scalar decoder, tabulated)."""
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float32)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
 def e4m3_value(code: int) -> float:
     return _load().oracle_e4m3_value(code)
 
