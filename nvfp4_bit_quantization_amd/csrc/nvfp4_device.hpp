@@ -50,22 +50,36 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // (first value in the low nibble) placed in byte `sel` of `old`.
 #define NVFP4_CVT_PK_FP4(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
 
-// Stochastic rounding with a 16-bit uniform: a' = min(|y|, 6) lies between grid
-// neighbours lo <= a' <= hi; round up iff u16 < 65536 * (a' - lo) / (hi - lo).
-// For a' >= 1 the grid points are the binary32 values with one mantissa bit:
-// a step is one unit of bit 22, and the low 22 bits d give the fraction d / 2^22,
-// so rounding up (d > 64 u16) is exactly a carry into bit 22 when 2^22 - 1 -
-// 64 u16 is added; the carry also crosses binades (1.5 -> 2, 3 -> 4).  Below 1
-// the spacing is 1/2: t = 2a' is exact and its fraction t - floor(t) is
-// compared in binary32 (exact).  Both forms are evaluated and one selected.
+// Stochastic rounding with a 16-bit uniform u16: a' = min(|y|, 6) lies between
+// grid neighbours lo <= a' <= hi, and rounds up iff u16 < 65536 (a' - lo) /
+// (hi - lo).  With an integer u16 that is the same as u16 < ceil(65536 f)
+// for the exact fraction f, i.e. a carry out of (ceil(65536 f) + 65535 - u16)
+// into bit 16.  Two exact forms of the sum, each valid on part of the range:
+//   * a' < 2, where the grid ordinal is 2a' (steps of 1/2):
+//     T = ceil(2^17 a') is computed exactly in binary32 (a power-of-two
+//     scaling, then a ceiling), and the code is (T + 65535 - u16) >> 16;
+//   * a' >= 1, where every grid point is a binary32 value with one mantissa
+//     bit: a step is one unit of bit 22 of the bit pattern, the low 22 bits d
+//     give f = d / 2^22, and the code is (bits(a') + 2^22 - 1 - 64 u16) >> 22
+//     less the ordinal offset of 1.0 (the carry also crosses binades).
+// Both sums are formed at the scale of bit 22 (the first as 64 T), offset so
+// that one constant finishes either: X_lo = 64 T + bits(2^16) and X_hi =
+// bits(2^17 a') = bits(a') + 17 * 2^23.  For a' < 1, X_hi <= X_lo <= bits(2^17);
+// for a' >= 1, bits(2^17) <= X_hi <= X_lo; so the median of the three picks
+// the right one (compared as positive binary32 values, i.e. as integers).
+// Then (u16 << 6) ^ 0xB8BFFFFF = 2^22 - 1 - 64 u16 - bits(2^16) (mod 2^32) is
+// added and bits 22.. give the magnitude code 0..7.
+__device__ __forceinline__ uint32_t e2m1_sr_mag(float y, uint32_t u16) {
+  const float a17 = fminf(fabsf(y * 131072.0f), 786432.0f);  // 2^17 a', exact
+  const uint32_t t = (uint32_t)__builtin_ceilf(a17);
+  const uint32_t x_lo = (t << 6) + 0x47800000u;
+  const float x = __builtin_amdgcn_fmed3f(__uint_as_float(x_lo), 131072.0f, a17);
+  return (((u16 << 6) ^ 0xB8BFFFFFu) + __float_as_uint(x)) >> 22;
+}
+
+// the full code: magnitude plus the sign bit of y (-0 gives 0x8)
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-  const uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
-  const float a = fminf(fabsf(y), 6.0f);
-  const uint32_t code_hi = ((__float_as_uint(a) + (0x3FFFFFu - (u16 << 6))) >> 22) - 252u;
-  const float t = a * 2.0f;
-  const float fr = __builtin_amdgcn_fractf(t);
-  const uint32_t code_lo = (uint32_t)t + (((float)u16 < fr * 65536.0f) ? 1u : 0u);
-  return (a >= 1.0f ? code_hi : code_lo) | sign;
+  return e2m1_sr_mag(y, u16) | ((__float_as_uint(y) >> 28) & 8u);
 }
 
 // -------------------------------------------------------------- Philox ----
@@ -75,8 +89,14 @@ __device__ __forceinline__ void philox4x32_10(uint32_t k0, uint32_t k1, uint32_t
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    uint32_t n0, n2;
+    if (r < 2) {  // the first rounds see the zero counter words: left to constant folding
+      n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+      n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    } else {  // three-way XOR in one instruction
+      n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+      n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
+    }
     c[1] = (uint32_t)p1;
     c[3] = (uint32_t)p0;
     c[0] = n0;

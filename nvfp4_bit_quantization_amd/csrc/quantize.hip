@@ -23,9 +23,19 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(AmaxArgs a) {
 }
 
 // Quantise pass: one micro-tile per lane, global scales from the partial
-// maxima of the amax pass.
+// maxima of the amax pass.  Instantiations with a column output in the RHT
+// domain are held to five waves per SIMD (at most 102 VGPRs), or four (128)
+// when stochastic rounding is involved: they fit without spilling, and the
+// extra waves hide more load latency than the larger register budget the
+// compiler would otherwise take buys (measured); the others keep their
+// allocation, which some of them need to avoid spills.
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
-__global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantArgs a) {
+constexpr int quant_waves_per_simd() {
+  return ((G0 == G_COL && RHT0) || (G1 == G_COL && RHT1)) ? ((SR0 || SR1) ? 4 : 5) : 1;
+}
+template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
+__global__ __launch_bounds__(kQThreads) __attribute__((
+    amdgpu_waves_per_eu(quant_waves_per_simd<G0, RHT0, SR0, G1, RHT1, SR1>()))) void quantize_kernel(QuantArgs a) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];

@@ -191,12 +191,21 @@ __device__ __forceinline__ uint32_t pack8_rtn(const float v[8], float rb) {
   return w;
 }
 
-// 8 values -> word, SR with the uniforms of draw w[] (value k uses u16_of(w, k))
+// 8 values -> word, SR with the uniforms of draw w[] (value k uses u16_of(w, k));
+// the sign bits come from the nearest-even conversion of the same values, which
+// keeps the sign of every value, zero included
 __device__ __forceinline__ uint32_t pack8_sr(const float v[8], float rb, const uint32_t w[4]) {
-  uint32_t word = 0;
+  float y[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) word |= e2m1_sr(v[k] * rb, u16_of(w, k)) << (4 * k);
-  return word;
+  for (int k = 0; k < 8; ++k) y[k] = v[k] * rb;
+  uint32_t mag = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) mag |= e2m1_sr_mag(y[k], u16_of(w, k)) << (4 * k);
+  uint32_t sgn = NVFP4_CVT_PK_FP4(0u, y[0], y[1], 0);
+  sgn = NVFP4_CVT_PK_FP4(sgn, y[2], y[3], 1);
+  sgn = NVFP4_CVT_PK_FP4(sgn, y[4], y[5], 2);
+  sgn = NVFP4_CVT_PK_FP4(sgn, y[6], y[7], 3);
+  return mag | (sgn & 0x88888888u);
 }
 
 __device__ __forceinline__ float block_scale(float bmax, float S, const float *lut, uint32_t *code) {
