@@ -15,6 +15,11 @@ versions), paragraph 2: E2M1 elements in 16-element blocks with E4M3 block
 scales and an FP32 per-tensor scale; 16x16 RHT with random signs on Wgrad
 inputs; 2D block scaling for weights; stochastic rounding for gradients.
 
+MXFP4 (the earlier microscaling format the page compares NVFP4 with, paragraph
+3) follows the OCP Microscaling Formats (MX) specification v1.0, since the page
+does not define it: 32-element blocks, E8M0 scale 2^(floor(log2 amax) - 2),
+E2M1 elements rounded to nearest-even and clamped at 6.
+
 Parity unpinned (conventions with no value on the page to pin them): nibble
 order, code and scale layouts, the Philox counter assignment for stochastic
 rounding and for the sign vector, and the block order.
@@ -85,6 +90,11 @@ def _load():
         "oracle_philox_array": (None, [P, P, i64, P]),
         "oracle_f64_to_bf16_array": (None, [P, i64, P]),
         "oracle_sr_uniform_array": (None, [u64, P, P, i64, P]),
+        "oracle_e8m0_scale_code": (ctypes.c_uint8, [f64]),
+        "oracle_e8m0_value": (f64, [ctypes.c_uint8]),
+        "oracle_mx_quantize": (i32, [P, i64, i64, i64, i32, P, P]),
+        "oracle_mx_decode": (i32, [P, P, i64, i64, P]),
+        "oracle_mx_gemm_f64": (i32, [P, P, P, P, i64, i64, i64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -295,3 +305,65 @@ def round_output(c64: np.ndarray, out_dtype: str) -> np.ndarray:
     if out_dtype == "bf16":
         return bf16_bits_to_f32(f64_to_bf16_bits(c64))
     raise ValueError(out_dtype)
+
+
+# --------------------------------------------------------------------------
+# MXFP4 (OCP MX v1.0): 32-element blocks with an E8M0 scale
+# --------------------------------------------------------------------------
+def e8m0_scale_code(amax: float) -> int:
+    return int(_load().oracle_e8m0_scale_code(float(amax)))
+
+
+def e8m0_value(code: int) -> float:
+    return float(_load().oracle_e8m0_value(code))
+
+
+def mx_quantize(x_bits: np.ndarray, layout="row") -> Dict:
+    """MXFP4 quantisation of a bf16 tensor (uint16 bit patterns [R][C]); layout
+    'row' (blocks along C, output [R][C]) or 'col' (blocks along R, output
+    [C][R]).  Returns dict(codes [orow][ocol/2], scales [orow][ocol/32] E8M0,
+    rows, cols)."""
+    layout = LAYOUTS.get(layout, layout)
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x_bits.shape
+    orow, ocol = out_shape(R, C, layout)
+    codes = np.zeros((orow, ocol // 2), dtype=np.uint8)
+    scales = np.zeros((orow, max(ocol // 32, 1)), dtype=np.uint8)
+    rc = _load().oracle_mx_quantize(_ptr(x_bits), R, C, C, layout, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle_mx_quantize rejected the arguments (rc=%d)" % rc)
+    return dict(codes=codes, scales=scales, rows=orow, cols=ocol)
+
+
+def mx_decode(q: Dict) -> np.ndarray:
+    """Exact element values e(code) * 2^(scale - 127) as float64."""
+    codes = np.ascontiguousarray(q["codes"], dtype=np.uint8)
+    scales = np.ascontiguousarray(q["scales"], dtype=np.uint8)
+    out = np.empty((q["rows"], q["cols"]), dtype=np.float64)
+    rc = _load().oracle_mx_decode(_ptr(codes), _ptr(scales), q["rows"], q["cols"], _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_mx_decode rejected the arguments (rc=%d)" % rc)
+    return out
+
+
+def mx_gemm_f64_loop(qa: Dict, qb: Dict) -> np.ndarray:
+    """C = A^ B^T by the plain triple loop in binary64 (small shapes)."""
+    M, K = qa["rows"], qa["cols"]
+    N = qb["rows"]
+    assert qb["cols"] == K
+    c = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_mx_gemm_f64(_ptr(np.ascontiguousarray(qa["codes"])), _ptr(np.ascontiguousarray(qa["scales"])),
+                                    _ptr(np.ascontiguousarray(qb["codes"])), _ptr(np.ascontiguousarray(qb["scales"])),
+                                    M, N, K, _ptr(c))
+    if rc != 0:
+        raise ValueError("oracle_mx_gemm_f64 rejected the arguments (rc=%d)" % rc)
+    return c
+
+
+def mx_gemm_f64(qa: Dict, qb: Dict, rows_a=None) -> np.ndarray:
+    """C = A^ B^T in binary64 via a float64 BLAS matmul on the exactly decoded
+    operands (optionally only the rows ``rows_a`` of A)."""
+    A = mx_decode(qa)
+    if rows_a is not None:
+        A = A[np.asarray(rows_a)]
+    return A @ mx_decode(qb).T

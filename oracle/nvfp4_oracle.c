@@ -438,6 +438,96 @@ int oracle_gemm_f64(const uint8_t *a_codes, const uint8_t *a_scales, int a_kind,
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP4, the earlier 4-bit microscaling format the page sets NVFP4 against  */
+/* (paragraph 3).  The page gives no definition of it; the one followed here  */
+/* is the OCP Microscaling Formats (MX) specification v1.0 (section 5: MX     */
+/* block of k = 32 elements, E8M0 shared scale, FP4 E2M1 elements; section    */
+/* 6.3: conversion).  Per block of 32 consecutive elements along the          */
+/* contiguous (K) dimension of the output orientation:                        */
+/*   e = floor(log2(max |v|)) - 2  (2 = exponent of 4, the largest power of    */
+/*       two of E2M1), clamped to the E8M0 range [-127, 127];                 */
+/*   X = 2^e, stored as the E8M0 code e + 127;                                */
+/*   element = v / X rounded to the nearest E2M1 value, ties to even, values  */
+/*       above 6 clamped to 6 (the E2M1 RTN encoder above), sign kept.       */
+/* Readings: an all-zero block takes the smallest scale 2^-127 (code 0); the  */
+/* code 0xFF (NaN) is never produced (inputs are finite).                     */
+/* Pinned by hand-computed codes, brute-force scale and grid searches, the    */
+/* block-maximum invariant and an exact rational GEMM on small inputs.        */
+/* ------------------------------------------------------------------------ */
+uint8_t oracle_e8m0_scale_code(double amax) {
+  if (!(amax > 0.0)) return 0;
+  int fe;
+  frexp(amax, &fe); /* amax = f 2^fe, f in [0.5, 1): floor(log2 amax) = fe - 1 */
+  int e = fe - 1 - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return (uint8_t)(e + 127);
+}
+
+double oracle_e8m0_value(uint8_t code) { return ldexp(1.0, (int)code - 127); }
+
+/* layout OR_ROW_1D: blocks along C, output [R][C]; OR_COL_1D: blocks along R,
+ * output x^T [C][R].  codes [orow][ocol/2] (element 2i in the low nibble),
+ * scales [orow][ocol/32].  The blocked dimension must be a multiple of 32.
+ * Returns 0, or -1 for unsupported arguments. */
+int oracle_mx_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int layout, uint8_t *codes,
+                       uint8_t *scales) {
+  if (R <= 0 || C <= 0 || ld < C) return -1;
+  if (layout != OR_ROW_1D && layout != OR_COL_1D) return -1;
+  const int64_t orow = layout == OR_ROW_1D ? R : C, ocol = layout == OR_ROW_1D ? C : R;
+  if (ocol % 32) return -1;
+  memset(codes, 0, (size_t)(orow * (ocol / 2)));
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < orow; r++)
+    for (int64_t b = 0; b < ocol / 32; b++) {
+      double v[32], amax = 0.0;
+      for (int j = 0; j < 32; j++) {
+        const int64_t c = b * 32 + j;
+        v[j] = layout == OR_ROW_1D ? (double)v_at(x, ld, r, c) : (double)v_at(x, ld, c, r);
+        if (fabs(v[j]) > amax) amax = fabs(v[j]);
+      }
+      const uint8_t sc = oracle_e8m0_scale_code(amax);
+      scales[r * (ocol / 32) + b] = sc;
+      const double X = oracle_e8m0_value(sc);
+      for (int j = 0; j < 32; j++) {
+        /* v / X is exact in binary64; in binary32 it can only lose bits when
+         * it is below 2^-126, where every value encodes to a signed zero */
+        const uint8_t code = oracle_e2m1_encode_rtn((float)(v[j] / X));
+        const int64_t c = b * 32 + j;
+        codes[r * (ocol / 2) + c / 2] |= (uint8_t)((c & 1) ? (code << 4) : code);
+      }
+    }
+  return 0;
+}
+
+/* x^ = e(code) * X, exact in binary64 */
+int oracle_mx_decode(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, double *out) {
+  if (rows <= 0 || cols <= 0 || (cols % 32)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t c = 0; c < cols; c++)
+      out[r * cols + c] = oracle_e2m1_value(code_at(codes, cols, r, c)) * oracle_e8m0_value(scales[r * (cols / 32) + c / 32]);
+  return 0;
+}
+
+/* C[m][n] = sum_k A^[m][k] B^[n][k], both operands K-contiguous; binary64
+ * triple loop (every product exact) */
+int oracle_mx_gemm_f64(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                       const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, double *c) {
+  if (M <= 0 || N <= 0 || K <= 0 || (K % 32)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t nn = 0; nn < N; nn++) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; k++)
+        acc += oracle_e2m1_value(code_at(a_codes, K, m, k)) * oracle_e8m0_value(a_scales[m * (K / 32) + k / 32]) *
+               oracle_e2m1_value(code_at(b_codes, K, nn, k)) * oracle_e8m0_value(b_scales[nn * (K / 32) + k / 32]);
+      c[m * N + nn] = acc;
+    }
+  return 0;
+}
+
 /* Round a binary64 value to the nearest bf16 (ties to even), returning the
  * bit pattern; one rounding straight from binary64. */
 uint16_t oracle_f64_to_bf16(double x) {
