@@ -177,6 +177,61 @@ uint16_t nvfp4_rht_sign_mask(uint64_t rht_seed);
 /* Host: a static description of a status code. */
 const char *nvfp4_status_string(int status);
 
+/* ------------------------------------------------------------------------
+ * MXFP4, the earlier 4-bit microscaling format the page sets NVFP4 against
+ * (paragraph 3: its loss gap to BF16 and the extra tokens it needs).  The page
+ * does not define it; these entry points follow the OCP Microscaling Formats
+ * (MX) specification v1.0 (section 5: blocks of 32 elements sharing an E8M0
+ * scale, FP4 E2M1 elements; section 6.3: conversion):
+ *   per block of 32 along the blocked (K) dimension:
+ *     e = floor(log2(max |v|)) - 2, clamped to [-127, 127]; X = 2^e, stored as
+ *     the E8M0 byte e + 127 (an all-zero block: byte 0);
+ *     element = v / X rounded to nearest, ties to even, onto the E2M1 grid,
+ *     values above 6 clamped to 6, sign kept (-0 gives code 8).
+ *   dequantised value = e(code) * X.  There is no per-tensor scale: one pass.
+ * Storage: codes as for NVFP4 ([rows][cols/2], element 2i in the low nibble);
+ * scales [rows][cols/32] E8M0 bytes.  The GEMM runs on the gfx950 block-scaled
+ * FP4 matrix instruction, which applies the 32-element E8M0 scales itself.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  uint8_t *codes;   /* [rows][cols/2] packed E2M1 */
+  uint8_t *scales;  /* [rows][cols/32] E8M0 */
+  int64_t rows;
+  int64_t cols;     /* blocked (K) dimension, a multiple of 32 */
+} mxfp4_tensor;
+
+/*
+ * mxfp4_quantize -- quantise x (bf16, [rows][cols], row stride ld_x) into out.
+ * Defines: page paragraph 3 names the format; the OCP MX specification v1.0
+ * defines it (see above).
+ *   x       device, bf16, 16-byte aligned, ld_x >= cols, ld_x % 8 == 0
+ *   layout  NVFP4_ROW_1D (blocks along cols; out is rows x cols) or
+ *           NVFP4_COL_1D (blocks along rows; out is x^T, cols x rows)
+ *   rows, cols  the blocked dimension a multiple of 32, the other of 16
+ *   out     device buffers of the stored shape; codes 16-byte aligned
+ * Enqueues one kernel; writes out->codes and out->scales.
+ */
+int mxfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int32_t layout, const mxfp4_tensor *out,
+                   void *stream);
+
+/*
+ * mxfp4_dequantize -- y[r][c] = e(code) * X for the stored orientation of q,
+ * fp32 with row stride ld_y (y 16-byte aligned, ld_y >= q->cols,
+ * ld_y % 4 == 0; q->codes 16-byte aligned; q->cols a multiple of 32).
+ */
+int mxfp4_dequantize(const mxfp4_tensor *q, float *y, int64_t ld_y, void *stream);
+
+/*
+ * mxfp4_gemm -- C[m][n] = sum_k A^[m][k] * B^[n][k], A^ = e(code) * X.
+ *   a : M x K, b : N x K (a->cols == b->cols = K, a multiple of 32)
+ *   c : device, [M][N] with row stride ldc >= N, fp32 or bf16 (RNE)
+ *   codes 16-byte aligned, scales 4-byte aligned, c 16-byte aligned
+ * FP4 codes and E8M0 scales go to the MFMA unchanged; fp32 accumulation.
+ * M, N multiples of 256 and K of 128 take the LDS-pipelined 256x256 kernel;
+ * other shapes a direct kernel with zero-filled edges.
+ */
+int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *stream);
+
 /*
  * Codec self-test hooks (for the exhaustive hardware checks in the tests):
  * run the device's element/scale encoders exactly as the quantise kernels use

@@ -43,6 +43,11 @@ class nvfp4_tensor(ctypes.Structure):
                 ("scale_kind", ctypes.c_int32), ("rht", ctypes.c_int32)]
 
 
+class mxfp4_tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
+
+
 class nvfp4_quant_output(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("rounding", ctypes.c_int32), ("rht", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
@@ -79,6 +84,12 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_codec_selftest.restype = i32
     L.nvfp4_codec_selftest.argtypes = [i32, P, P, P, i64, P]
+    L.mxfp4_quantize.restype = i32
+    L.mxfp4_quantize.argtypes = [P, i64, i64, i64, ctypes.c_int32, ctypes.POINTER(mxfp4_tensor), P]
+    L.mxfp4_dequantize.restype = i32
+    L.mxfp4_dequantize.argtypes = [ctypes.POINTER(mxfp4_tensor), P, i64, P]
+    L.mxfp4_gemm.restype = i32
+    L.mxfp4_gemm.argtypes = [ctypes.POINTER(mxfp4_tensor), ctypes.POINTER(mxfp4_tensor), P, ctypes.c_int32, i64, P]
     _lib = L
     return L
 
@@ -263,3 +274,71 @@ def gemm(a: QTensor, b: QTensor, out_dtype="f32", workspace=None, stream=None):
     dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
     c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
     return nvfp4_gemm(a, b, c, workspace, stream)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP MX v1.0: 32-element blocks, E8M0 scales, no per-tensor scale)
+# ---------------------------------------------------------------------------
+@dataclass
+class MXTensor:
+    codes: "object"   # torch.uint8 [rows][cols/2]
+    scales: "object"  # torch.uint8 [rows][cols/32] (E8M0)
+    rows: int
+    cols: int
+
+    def c_struct(self) -> mxfp4_tensor:
+        return mxfp4_tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.cols)
+
+
+def empty_mxtensor(rows: int, cols: int, device="cuda") -> MXTensor:
+    import torch
+    return MXTensor(codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                    scales=torch.empty((rows, cols // 32), dtype=torch.uint8, device=device), rows=rows, cols=cols)
+
+
+def mxfp4_quantize(x, layout, out: MXTensor, stream=None) -> MXTensor:
+    """MXFP4-quantise the bf16 device tensor x [rows][cols] into out
+    (layout ROW_1D: out is rows x cols; COL_1D: out is x^T)."""
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    t = out.c_struct()
+    _check(lib().mxfp4_quantize(ctypes.c_void_p(x.data_ptr()), x.shape[0], x.shape[1], x.stride(0),
+                                LAYOUTS.get(layout, layout), ctypes.byref(t), _stream(stream)), "mxfp4_quantize")
+    return out
+
+
+def mxfp4_dequantize(q: MXTensor, y, stream=None):
+    """y = e(code) * 2^(scale - 127) as fp32."""
+    import torch
+    assert y.dtype == torch.float32 and y.stride(1) == 1
+    t = q.c_struct()
+    _check(lib().mxfp4_dequantize(ctypes.byref(t), ctypes.c_void_p(y.data_ptr()), y.stride(0), _stream(stream)),
+           "mxfp4_dequantize")
+    return y
+
+
+def mxfp4_gemm(a: MXTensor, b: MXTensor, c, stream=None):
+    """C[M][N] = A^ B^T into the fp32 or bf16 device tensor c."""
+    import torch
+    dt = F32 if c.dtype == torch.float32 else BF16 if c.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("c must be float32 or bfloat16")
+    assert c.stride(1) == 1
+    ta, tb = a.c_struct(), b.c_struct()
+    _check(lib().mxfp4_gemm(ctypes.byref(ta), ctypes.byref(tb), ctypes.c_void_p(c.data_ptr()), dt, c.stride(0),
+                            _stream(stream)), "mxfp4_gemm")
+    return c
+
+
+def mx_quantize(x, layout="row", stream=None) -> MXTensor:
+    """Allocate the output and MXFP4-quantise x."""
+    layout = LAYOUTS.get(layout, layout)
+    r, c = (x.shape[0], x.shape[1]) if layout == ROW_1D else (x.shape[1], x.shape[0])
+    return mxfp4_quantize(x, layout, empty_mxtensor(r, c, x.device), stream)
+
+
+def mx_gemm(a: MXTensor, b: MXTensor, out_dtype="f32", stream=None):
+    import torch
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
+    return mxfp4_gemm(a, b, c, stream)

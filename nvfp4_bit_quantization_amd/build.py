@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4.so")
-SOURCES = ["quantize.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "mxfp4.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -266,6 +266,70 @@ int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_
   return finish(launch_gemm(g, workspace, workspace_bytes, s), s);
 }
 
+// ---------------------------------------------------------------- MXFP4 ----
+int mxfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, int32_t layout, const mxfp4_tensor *out,
+                   void *stream) {
+  if (!x || !out || !out->codes || !out->scales) return NVFP4_E_NULL;
+  if (layout != NVFP4_ROW_1D && layout != NVFP4_COL_1D) return NVFP4_E_UNSUPPORTED;
+  const int64_t orow = layout == NVFP4_ROW_1D ? rows : cols, ocol = layout == NVFP4_ROW_1D ? cols : rows;
+  if (rows <= 0 || cols <= 0 || (ocol % 32) || (orow % 16)) return NVFP4_E_SHAPE;
+  if (out->rows != orow || out->cols != ocol) return NVFP4_E_SHAPE;
+  if (ld_x < cols) return NVFP4_E_LD;
+  if (!aligned16(x) || (ld_x % 8) || !aligned16(out->codes)) return NVFP4_E_ALIGN;
+  if ((rows / 128 + 1) * (cols / 256 + 1) >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+  MxQuantArgs a;
+  a.x = static_cast<const uint16_t *>(x);
+  a.R = rows;
+  a.C = cols;
+  a.ld = ld_x;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_mx_quantize(a, layout == NVFP4_ROW_1D ? G_ROW : G_COL, s), s);
+}
+
+int mxfp4_dequantize(const mxfp4_tensor *q, float *y, int64_t ld_y, void *stream) {
+  if (!q || !y || !q->codes || !q->scales) return NVFP4_E_NULL;
+  if (q->rows <= 0 || q->cols <= 0 || (q->cols % 32)) return NVFP4_E_SHAPE;
+  if (ld_y < q->cols) return NVFP4_E_LD;
+  if (!aligned16(y) || (ld_y % 4) || !aligned16(q->codes)) return NVFP4_E_ALIGN;
+  MxDequantArgs a;
+  a.codes = q->codes;
+  a.scales = q->scales;
+  a.y = y;
+  a.rows = q->rows;
+  a.cols = q->cols;
+  a.ld_y = ld_y;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_mx_dequantize(a, s), s);
+}
+
+int mxfp4_gemm(const mxfp4_tensor *a, const mxfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *stream) {
+  if (!a || !b || !c || !a->codes || !a->scales || !b->codes || !b->scales) return NVFP4_E_NULL;
+  if (a->rows <= 0 || b->rows <= 0 || a->cols <= 0 || (a->cols % 32)) return NVFP4_E_SHAPE;
+  if (a->cols != b->cols) return NVFP4_E_UNSUPPORTED;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_E_UNSUPPORTED;
+  if (ldc < b->rows) return NVFP4_E_LD;
+  if (!aligned16(a->codes) || !aligned16(b->codes) || !aligned16(c) || ((uintptr_t)a->scales & 3u) ||
+      ((uintptr_t)b->scales & 3u))
+    return NVFP4_E_ALIGN;
+  if (a->rows > ((int64_t)1 << 31) || b->rows > ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+  if (((a->rows + 127) / 128) * ((b->rows + 127) / 128) >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+  MxGemmArgs g;
+  g.a_codes = a->codes;
+  g.a_scales = a->scales;
+  g.b_codes = b->codes;
+  g.b_scales = b->scales;
+  g.c = c;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->cols;
+  g.ldc = ldc;
+  g.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_mx_gemm(g, s), s);
+}
+
 int nvfp4_codec_selftest(int which, const float *in_f32, const uint16_t *in_u16, uint8_t *out_u8, int64_t n,
                          void *stream) {
   if (which < 0 || which > 2) return NVFP4_E_UNSUPPORTED;

@@ -18,6 +18,7 @@
 // dword of codes at byte 16h + 4s of the row's 32-byte K-tile slice, under the
 // block scale of k-block 2h + s/2.  A and B use the same mapping, so every k
 // of the tile is summed exactly once.
+#include "gemm_device.hpp"
 #include "nvfp4_device.hpp"
 #include "nvfp4_kernels.hpp"
 
@@ -246,24 +247,6 @@ constexpr int kFBK = 128;
 constexpr int kFStageCodes = 512 * 64;         // bytes of codes per stage
 constexpr int kFStageBytes = kFStageCodes + 512 * 8;
 constexpr int kFStages = 3;
-constexpr uint32_t kGroupM = 4;  // tile rows per group of the tile order
-
-__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(size_t)(lds_void_t *)p; }
-
-// one wave-wide direct transfer: lane l's 16 (4) bytes at base + voff land at
-// LDS byte lds + 16 l (4 l)
-__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
-}
-
-// vmcnt <= n (other counters untouched)
-#define NVFP4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 struct FastCtx {
   const uint8_t *cbase;  // codes of the operand this wave transfers (A: waves 0-1, B: waves 2-3)
@@ -291,9 +274,6 @@ __device__ __forceinline__ void fast_issue(const FastCtx &c, uint32_t lds_stage,
            __builtin_amdgcn_readfirstlane(lds_stage + kFStageCodes + (wave * 4 + (t - 8)) * 256u));
   }
 }
-
-// lgkmcnt <= 0 (LDS reads of this wave complete; other counters untouched)
-#define NVFP4_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 // The fp16 MFMA operands of one sub-step (16 k): 4 A and 4 B fragments.
 struct Frags {
@@ -333,16 +313,6 @@ __device__ __forceinline__ void interleave_step() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
   }
-}
-
-// origin of tile t of the grouped order (see gemm_fast_kernel)
-__device__ __forceinline__ void tile_origin(const GemmArgs &g, uint32_t tile, int64_t &m0, int64_t &n0) {
-  const uint32_t tiles_m = (uint32_t)(g.M / 256), tiles_n = (uint32_t)(g.N / 256);
-  const uint32_t group = tile / (kGroupM * tiles_n), first_m = group * kGroupM;
-  const uint32_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
-  const uint32_t local = tile - group * kGroupM * tiles_n;
-  m0 = (int64_t)(first_m + local % gm) * 256;
-  n0 = (int64_t)(local / gm) * 256;
 }
 
 // Accumulate K-tiles [ka, kb) of the 256x256 C tile at (m0, n0) into acc.
@@ -583,7 +553,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
   // that one XCD runs at a time cover a compact block of C: they share the A
   // and B K-slices in that XCD's L2 instead of each streaming its own.
   int64_t m0, n0;
-  tile_origin(g, xcd_tile(blockIdx.x, gridDim.x), m0, n0);
+  tile_origin(g.M, g.N, xcd_tile(blockIdx.x, gridDim.x), m0, n0);
   float16v acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -674,7 +644,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_streamk_kernel(GemmArgs g, Str
   int64_t m0, n0;
 
   for (uint32_t t = w; t < sk.dp_tiles; t += G) {  // whole tiles, round by round
-    tile_origin(g, t, m0, n0);
+    tile_origin(g.M, g.N, t, m0, n0);
     zero_acc(acc);
     fast_tile(g, m0, n0, 0, sk.KT, acc, lds);
     fast_store_c(g, m0, n0, acc);
@@ -687,7 +657,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_streamk_kernel(GemmArgs g, Str
     const uint32_t ts = (uint32_t)(u / sk.KT), ka = (uint32_t)(u - (uint64_t)ts * sk.KT);
     const uint64_t tend = (uint64_t)(ts + 1) * sk.KT;
     const uint32_t kb = (uint32_t)((uend < tend ? uend : tend) - (uint64_t)ts * sk.KT);
-    tile_origin(g, sk.dp_tiles + ts, m0, n0);
+    tile_origin(g.M, g.N, sk.dp_tiles + ts, m0, n0);
     zero_acc(acc);
     fast_tile(g, m0, n0, ka, kb, acc, lds);
     if (ka > 0) {  // this range starts inside the tile: hand the partial to its head

@@ -81,6 +81,35 @@ struct GemmArgs {
   int c_bf16;
 };
 
+// MXFP4 (OCP MX v1.0): 32-element blocks with an E8M0 scale, no per-tensor scale
+struct MxQuantArgs {
+  const uint16_t *x;
+  int64_t R, C, ld;
+  uint8_t *codes;   // ROW: [R][C/2]; COL: [C][R/2]
+  uint8_t *scales;  // ROW: [R][C/32]; COL: [C][R/32]
+};
+
+struct MxDequantArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  float *y;
+  int64_t rows, cols, ld_y;
+};
+
+struct MxGemmArgs {
+  const uint8_t *a_codes;
+  const uint8_t *a_scales;
+  const uint8_t *b_codes;
+  const uint8_t *b_scales;
+  void *c;
+  int64_t M, N, K, ldc;
+  int c_bf16;
+};
+
+hipError_t launch_mx_quantize(const MxQuantArgs &a, int geom, hipStream_t s);
+hipError_t launch_mx_dequantize(const MxDequantArgs &a, hipStream_t s);
+hipError_t launch_mx_gemm(const MxGemmArgs &g, hipStream_t s);
+
 // host launchers (one per translation unit); return hipError_t of the launch
 hipError_t launch_amax(const AmaxArgs &a, bool plain, bool rht_col, bool rht_row, int nparts, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int g1, bool rht1, bool sr1,

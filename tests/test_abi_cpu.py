@@ -25,14 +25,14 @@ def L():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(nvfp4_\w+)\s*\(", src, flags=re.M)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b((?:nv|mx)fp4_\w+)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_workspace_bytes", "nvfp4_rht_sign_mask",
-              "nvfp4_status_string", "nvfp4_codec_selftest"):
+              "nvfp4_status_string", "nvfp4_codec_selftest", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm"):
         assert n in names
 
 
@@ -119,6 +119,41 @@ def test_dequantize_and_gemm_validation(L):
     assert L.nvfp4_codec_selftest(3, None, None, None, 0, None) == -5
     assert L.nvfp4_codec_selftest(0, None, None, None, -1, None) == -2
     assert L.nvfp4_codec_selftest(0, None, None, None, 5, None) == -1
+
+
+def _mx(rows, cols, codes=FAKE, scales=FAKE):
+    return nv.mxfp4_tensor(codes, scales, rows, cols)
+
+
+def test_mxfp4_argument_validation(L):
+    x = ctypes.c_void_p(FAKE)
+    q = lambda out, rows=64, cols=96, ld=96, layout=nv.ROW_1D, xx=x: L.mxfp4_quantize(  # noqa: E731
+        xx, rows, cols, ld, layout, ctypes.byref(out), None)
+    assert q(_mx(64, 96), xx=None) == -1
+    assert q(_mx(64, 96, codes=0)) == -1
+    assert q(_mx(40, 96), rows=40) == -2                       # rows % 16 (row layout)
+    assert q(_mx(96, 48), rows=48, layout=nv.COL_1D) == -2     # blocked rows % 32 (column layout)
+    assert q(_mx(64, 80), cols=80, ld=80) == -2                # cols % 32
+    assert q(_mx(96, 64)) == -2                                # descriptor is not the stored shape
+    assert q(_mx(64, 96), ld=64) == -3
+    assert q(_mx(64, 96), ld=100) == -4                        # ld % 8
+    assert q(_mx(64, 96), xx=ctypes.c_void_p(FAKE + 2)) == -4
+    assert q(_mx(64, 96, codes=FAKE + 8)) == -4
+    assert q(_mx(64, 96), layout=nv.TWO_D) == -5
+    y = ctypes.c_void_p(FAKE)
+    assert L.mxfp4_dequantize(None, y, 96, None) == -1
+    assert L.mxfp4_dequantize(ctypes.byref(_mx(64, 80)), y, 96, None) == -2
+    assert L.mxfp4_dequantize(ctypes.byref(_mx(64, 96)), y, 64, None) == -3
+    assert L.mxfp4_dequantize(ctypes.byref(_mx(64, 96)), y, 98, None) == -4
+    a, b, c = _mx(64, 96), _mx(48, 96), ctypes.c_void_p(FAKE)
+    g = lambda a_, b_, c_=c, dt=0, ldc=48: L.mxfp4_gemm(ctypes.byref(a_), ctypes.byref(b_), c_, dt, ldc, None)  # noqa
+    assert g(a, b, c_=None) == -1
+    assert g(a, _mx(48, 64)) == -5                             # K mismatch
+    assert g(_mx(64, 80), _mx(48, 80)) == -2                   # K % 32
+    assert g(a, b, dt=2) == -5
+    assert g(a, b, ldc=40) == -3
+    assert g(a, _mx(48, 96, scales=FAKE + 2)) == -4            # scales 4-byte aligned
+    assert g(_mx(64, 96, codes=FAKE + 4), b) == -4
 
 
 def test_status_strings(L):
