@@ -8,8 +8,11 @@ weight-gradient GEMM dW = dY^T X (5120x5120, K = 8192, fp32 out).  This is the
 workload on which both halves of the metric (quantise GB/s, Wgrad GEMM
 TFLOP/s) are quoted.  Other workloads (``--workload``): ``act_8192x5120``
 (row + column quantise of an activation), ``weight_5120x20480`` (2D + 2D_T),
-``tiny_256`` and ``linear_step_16384`` (Fprop/Dgrad/Wgrad of a 5120/20480
-two-layer FFN over 16384 tokens).
+``tiny_256``, ``linear_step_16384`` (Fprop/Dgrad/Wgrad of a 5120/20480
+two-layer FFN over 16384 tokens) and ``mx_wgrad_8192x5120`` (the same Wgrad
+step in MXFP4, the earlier microscaling format the page compares NVFP4 with:
+single-pass quantise of dY and X along tokens, GEMM on the block-scaled FP4
+MFMA; its roofline is against the FP4 matrix peak).
 
 Prints ONE JSON line.  ``value`` is whole-step throughput (GEMM flops of the
 step over the wall time per step, inputs resident in HBM); per-call times come
@@ -34,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -228,8 +232,35 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
                                   step="Fprop H,Y; Dgrad dH,dX; Wgrad dW2,dW1; 6 quantise calls"))
 
 
+def setup_mx_wgrad(nv, syn, tokens=8192, hidden=5120):
+    import torch
+    dy_bits, x_bits = syn.wgrad_8192x5120(tokens, hidden)
+    dy, x = dev_bf16(dy_bits), dev_bf16(x_bits)
+    q_dy, q_x = nv.empty_mxtensor(hidden, tokens), nv.empty_mxtensor(hidden, tokens)
+    c = torch.empty((hidden, hidden), dtype=torch.float32, device="cuda")
+    flops = 2.0 * hidden * hidden * tokens
+    mxbytes = tokens * hidden * 2 + tokens * hidden // 2 + tokens * hidden // 32
+
+    def step(t: Timer):
+        t.run("quantize_dY", lambda: nv.mxfp4_quantize(dy, nv.COL_1D, q_dy))
+        t.run("quantize_X", lambda: nv.mxfp4_quantize(x, nv.COL_1D, q_x))
+        t.run("gemm_wgrad", lambda: nv.mxfp4_gemm(q_dy, q_x, c))
+
+    info = dict(flops=flops, calls={
+        "quantize_dY": dict(kind="quantize", bytes=mxbytes),
+        "quantize_X": dict(kind="quantize", bytes=mxbytes),
+        "gemm_wgrad": dict(kind="gemm", flops=flops, peak=MFMA_FP4_PEAK_TFLOPS)},
+        dominant="gemm_wgrad", kernel="mx_gemm_fast_kernel",
+        sources=("mxfp4.hip", "gemm_device.hpp", "nvfp4_kernels.hpp"),
+        dtype="mxfp4 operands (E2M1, E8M0 per 32); fp32 quantise math; fp4 MFMA with block scales, fp32 accumulate",
+        config=dict(workload="mx_wgrad_8192x5120", tokens=tokens, hidden=hidden,
+                    quantize="dY, X MXFP4 along tokens (OCP MX: 32-element blocks, E8M0 scale, RNE), one pass each",
+                    gemm="dW = dY^T X, M=N=%d, K=%d, fp32 out, block-scaled FP4 MFMA" % (hidden, tokens)))
+    return step, info
+
+
 WORKLOADS = {"wgrad_8192x5120": setup_wgrad, "act_8192x5120": setup_act, "weight_5120x20480": setup_weight,
-             "tiny_256": setup_tiny, "linear_step_16384": setup_linear}
+             "tiny_256": setup_tiny, "linear_step_16384": setup_linear, "mx_wgrad_8192x5120": setup_mx_wgrad}
 
 
 # ---------------------------------------------------------------------------
@@ -256,6 +287,20 @@ def cpu_baseline(workload: str, syn):
                     kind="oracle",
                     sample="the whole Wgrad workload (dY, X 8192x5120): C oracle quantise (col+RHT, SR/RTN; "
                            "%d threads, %.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s)"
+                           % (qthreads, t1 - t0, blas_threads, t2 - t1))
+    if workload == "mx_wgrad_8192x5120":
+        dy, xx = syn.wgrad_8192x5120()
+        t0 = time.perf_counter()
+        qa = oracle.mx_quantize(dy, "col")
+        qb = oracle.mx_quantize(xx, "col")
+        t1 = time.perf_counter()
+        oracle.mx_gemm_f64(qa, qb)
+        t2 = time.perf_counter()
+        flops = 2.0 * 5120 * 5120 * 8192
+        return dict(value=flops / (t2 - t0) / 1e12, unit="TFLOP/s", cores=max(qthreads, blas_threads),
+                    kind="oracle",
+                    sample="the whole MXFP4 Wgrad workload (dY, X 8192x5120): C oracle MX quantise (%d threads, "
+                           "%.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s)"
                            % (qthreads, t1 - t0, blas_threads, t2 - t1))
     if workload in ("act_8192x5120", "weight_5120x20480", "tiny_256"):
         if workload == "act_8192x5120":
@@ -344,7 +389,8 @@ def main():
         ms = t.ms(name)
         if c["kind"] == "gemm":
             tf = c["flops"] / (ms * 1e-3) / 1e12
-            parts[name] = dict(ms=round(ms, 4), tflops=round(tf, 1), frac_mfma=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
+            parts[name] = dict(ms=round(ms, 4), tflops=round(tf, 1),
+                               frac_mfma=round(tf / c.get("peak", MFMA_F16_PEAK_TFLOPS), 4))
         else:
             gbs = c["bytes"] / (ms * 1e-3) / 1e9
             parts[name] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
@@ -354,11 +400,13 @@ def main():
     dms = t.ms(dom)
     if dc["kind"] == "gemm":
         achieved = dc["flops"] / (dms * 1e-3) / 1e12
-        src = source_hash("gemm.hip", "nvfp4_device.hpp", "nvfp4_kernels.hpp")
+        peak = dc.get("peak", MFMA_F16_PEAK_TFLOPS)
+        src = source_hash(*info.get("sources", ("gemm.hip", "gemm_device.hpp", "nvfp4_device.hpp",
+                                                "nvfp4_kernels.hpp")))
         traffic = read_traffic("gemm_" + args.workload, src)
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / MFMA_F16_PEAK_TFLOPS, 4), traffic=traffic, kernel="gemm_fast_kernel<4,4>",
-                    ms=round(dms, 4), source_hash=src)
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=traffic,
+                    kernel=info.get("kernel", "gemm_fast_kernel<4,4>"), ms=round(dms, 4), source_hash=src)
     else:
         achieved = dc["bytes"] / (dms * 1e-3) / 1e9
         src = source_hash("quantize.hip", "quantize_device.hpp", "nvfp4_device.hpp", "nvfp4_kernels.hpp")
@@ -390,7 +438,8 @@ def main():
         "metric": "NVFP4 quantize GB/s (% HBM peak); NVFP4 Wgrad GEMM TFLOP/s (% MFMA peak)",
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "nvfp4 operands; fp32/fp64 quantise math; fp16 MFMA, fp32 accumulate", "data": "synthetic",
+        "dtype": info.get("dtype", "nvfp4 operands; fp32 quantise math; fp16 MFMA, fp32 accumulate"),
+        "data": "synthetic",
         "config": info["config"], "quantize": quant, "calls": parts, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
