@@ -63,6 +63,9 @@ extern "C" {
 #define NVFP4_2D 2     /* 16x16 tiles; stored [rows][cols], scales [rows/16][cols/16] */
 #define NVFP4_2D_T 3   /* the NVFP4_2D results stored transposed [cols][rows], scales [cols/16][rows/16] */
 
+/* output flags (nvfp4_quant_output.flags) */
+#define NVFP4_AMAX_GIVEN 1 /* out.amax already holds the output's maximum (e.g. from nvfp4_gemm_amax) */
+
 /* rounding */
 #define NVFP4_RTN 0 /* nearest, ties to even mantissa bit */
 #define NVFP4_SR 1  /* stochastic, Philox4x32-10 keyed by sr_seed */
@@ -94,7 +97,7 @@ typedef struct {
   int32_t layout;     /* NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_2D, NVFP4_2D_T */
   int32_t rounding;   /* NVFP4_RTN or NVFP4_SR */
   int32_t rht;        /* 1: 16x16 RHT along the blocked dim; 1D layouts only */
-  int32_t reserved;   /* must be 0 */
+  int32_t flags;      /* 0 or NVFP4_AMAX_GIVEN */
   uint64_t sr_seed;   /* Philox key of the stochastic rounding */
   uint64_t rht_seed;  /* Philox key of the RHT sign vector */
   nvfp4_tensor out;
@@ -116,7 +119,11 @@ typedef struct {
  *              16-byte aligned (per-workgroup partial maxima of the amax pass;
  *              no initialisation needed).  Calls that may run concurrently
  *              (different streams) need separate workspaces.
- * Enqueues two kernels (amax pass, quantise pass) on `stream`.
+ * Enqueues two kernels (amax pass, quantise pass) on `stream`.  With
+ * flags = NVFP4_AMAX_GIVEN, *out.amax must already hold max |v| of what that
+ * output quantises (the RHT-domain maximum for an RHT output, as
+ * nvfp4_gemm_amax produces it); the amax pass skips that output's maximum and
+ * is not launched at all when no output needs it (one kernel).
  * Writes codes, scales, *global_scale and *amax of every output.
  * RHT signs: d_j = -1 iff bit (j mod 16) of nvfp4_rht_sign_mask(rht_seed),
  * j the index along the blocked dimension.
@@ -165,6 +172,29 @@ int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream
  */
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *workspace,
                size_t workspace_bytes, void *stream);
+
+/*
+ * nvfp4_gemm_amax -- nvfp4_gemm with bf16 output that also produces the
+ * per-tensor maxima the quantisation of C needs (producer-fused amax: the
+ * quantiser can then skip its read of C for the amax).
+ * Defines: page paragraph 2 (the FP32 per-tensor scale, whose amax this is,
+ * and the RHT on Wgrad inputs: C's column quantisation along its rows).
+ *   a, b, c, ldc, workspace, workspace_bytes: as nvfp4_gemm, c bf16 (RNE)
+ *   amax_plain    device float or NULL: becomes max(*amax_plain, max |c|)
+ *                 over the stored bf16 values -- the amax of a ROW_1D, COL_1D,
+ *                 2D or 2D_T quantisation of C without RHT;
+ *   amax_rht_col  device float or NULL: becomes max(*amax_rht_col, max |z|)
+ *                 with z the 16x16 RHT (signs from rht_seed) of every aligned
+ *                 16-row group of C -- the amax of a COL_1D + RHT quantisation
+ *                 of C (rows are its blocked dimension).  Summed on the bf16
+ *                 MFMA, so it may differ from the quantiser's own binary32
+ *                 butterflies in the last bits (RHT tolerance).
+ * Both maxima are combined with device-scope atomic maxima, so the caller
+ * initialises them (0 for a fresh tensor).  At least one must be non-NULL;
+ * both 4-byte aligned.
+ */
+int nvfp4_gemm_amax(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int64_t ldc, void *workspace,
+                    size_t workspace_bytes, float *amax_plain, float *amax_rht_col, uint64_t rht_seed, void *stream);
 
 /* Bytes of GEMM workspace for the current device (8 KiB of flags plus one
  * 256 KiB fp32 tile per compute unit; 0 if no device is visible). */

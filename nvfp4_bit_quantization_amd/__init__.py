@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
 NVFP4_OK = 0
 ROW_1D, COL_1D, TWO_D, TWO_D_T = 0, 1, 2, 3
 RTN, SR = 0, 1
+AMAX_GIVEN = 1  # nvfp4_quant_output.flags
 SCALE_1D16, SCALE_2D16 = 0, 1
 F32, BF16 = 0, 1
 LAYOUTS = {"row": ROW_1D, "col": COL_1D, "2d": TWO_D, "2d_t": TWO_D_T}
@@ -50,7 +51,7 @@ class mxfp4_tensor(ctypes.Structure):
 
 class nvfp4_quant_output(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("rounding", ctypes.c_int32), ("rht", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
+                ("flags", ctypes.c_int32), ("sr_seed", ctypes.c_uint64), ("rht_seed", ctypes.c_uint64),
                 ("out", nvfp4_tensor)]
 
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_gemm.restype = i32
     L.nvfp4_gemm.argtypes = [ctypes.POINTER(nvfp4_tensor), ctypes.POINTER(nvfp4_tensor), P, ctypes.c_int32, i64, P,
                              ctypes.c_size_t, P]
+    L.nvfp4_gemm_amax.restype = i32
+    L.nvfp4_gemm_amax.argtypes = [ctypes.POINTER(nvfp4_tensor), ctypes.POINTER(nvfp4_tensor), P, i64, P,
+                                  ctypes.c_size_t, P, P, ctypes.c_uint64, P]
     L.nvfp4_gemm_workspace_bytes.restype = ctypes.c_size_t
     L.nvfp4_gemm_workspace_bytes.argtypes = []
     L.nvfp4_rht_sign_mask.restype = ctypes.c_uint16
@@ -145,10 +149,12 @@ class QuantSpec:
     rht: bool = False
     sr_seed: int = 0
     rht_seed: int = 0
+    amax_given: bool = False  # the output's amax tensor already holds its maximum (nvfp4_gemm_amax)
 
     @staticmethod
-    def of(layout="row", rounding="rtn", rht=False, sr_seed=0, rht_seed=0) -> "QuantSpec":
-        return QuantSpec(LAYOUTS.get(layout, layout), ROUNDINGS.get(rounding, rounding), bool(rht), sr_seed, rht_seed)
+    def of(layout="row", rounding="rtn", rht=False, sr_seed=0, rht_seed=0, amax_given=False) -> "QuantSpec":
+        return QuantSpec(LAYOUTS.get(layout, layout), ROUNDINGS.get(rounding, rounding), bool(rht), sr_seed, rht_seed,
+                         bool(amax_given))
 
 
 def output_shape(rows: int, cols: int, layout: int):
@@ -181,7 +187,8 @@ def nvfp4_quantize(x, specs: Sequence[QuantSpec], outs: Sequence[QTensor], works
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
     arr = (nvfp4_quant_output * len(specs))()
     for i, (s, o) in enumerate(zip(specs, outs)):
-        arr[i] = nvfp4_quant_output(s.layout, s.rounding, int(s.rht), 0, s.sr_seed, s.rht_seed, o.c_struct())
+        arr[i] = nvfp4_quant_output(s.layout, s.rounding, int(s.rht), AMAX_GIVEN if s.amax_given else 0, s.sr_seed,
+                                    s.rht_seed, o.c_struct())
     st = lib().nvfp4_quantize(ctypes.c_void_p(x.data_ptr()), x.shape[0], x.shape[1], x.stride(0), arr, len(specs),
                               ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
                               _stream(stream))
@@ -212,6 +219,25 @@ def nvfp4_gemm(a: QTensor, b: QTensor, c, workspace=None, stream=None):
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().nvfp4_gemm(ctypes.byref(ta), ctypes.byref(tb), ctypes.c_void_p(c.data_ptr()), dt, c.stride(0),
                             wp, wb, _stream(stream)), "nvfp4_gemm")
+    return c
+
+
+def nvfp4_gemm_amax(a: QTensor, b: QTensor, c, amax_plain=None, amax_rht_col=None, rht_seed: int = 0,
+                    workspace=None, stream=None):
+    """nvfp4_gemm into the bf16 tensor c that also folds max |c| into the
+    float32 device tensor amax_plain[0] and the RHT-domain maximum of c's
+    16-row groups (signs from rht_seed) into amax_rht_col[0] (atomic maxima:
+    initialise them, e.g. to 0)."""
+    import torch
+    if c.dtype != torch.bfloat16:
+        raise TypeError("c must be bfloat16")
+    assert c.stride(1) == 1
+    ta, tb = a.c_struct(), b.c_struct()
+    p = (lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0))
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().nvfp4_gemm_amax(ctypes.byref(ta), ctypes.byref(tb), ctypes.c_void_p(c.data_ptr()), c.stride(0),
+                                 p(workspace), wb, p(amax_plain), p(amax_rht_col), rht_seed, _stream(stream)),
+           "nvfp4_gemm_amax")
     return c
 
 

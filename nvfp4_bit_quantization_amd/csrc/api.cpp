@@ -60,7 +60,7 @@ struct OutPlan {
 
 // validate one output descriptor against the input shape; fill its plan
 int plan_output(const nvfp4_quant_output &o, int64_t R, int64_t C, OutPlan *p) {
-  if (o.reserved != 0) return NVFP4_E_UNSUPPORTED;
+  if (o.flags != 0 && o.flags != NVFP4_AMAX_GIVEN) return NVFP4_E_UNSUPPORTED;
   if (o.rounding != NVFP4_RTN && o.rounding != NVFP4_SR) return NVFP4_E_UNSUPPORTED;
   if (o.rht != 0 && o.rht != 1) return NVFP4_E_UNSUPPORTED;
   const nvfp4_tensor &t = o.out;
@@ -83,12 +83,51 @@ int plan_output(const nvfp4_quant_output &o, int64_t R, int64_t C, OutPlan *p) {
   return NVFP4_OK;
 }
 
+// host-side validation shared by nvfp4_gemm and nvfp4_gemm_amax
+int gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, const void *c, int32_t c_dtype, int64_t ldc,
+               const void *workspace) {
+  if (!a || !b || !c) return NVFP4_E_NULL;
+  if (!a->codes || !a->scales || !a->global_scale || !b->codes || !b->scales || !b->global_scale) return NVFP4_E_NULL;
+  if (a->rows <= 0 || b->rows <= 0 || a->cols <= 0 || (a->rows % 16) || (b->rows % 16) || (a->cols % 16))
+    return NVFP4_E_SHAPE;
+  if (a->cols != b->cols) return NVFP4_E_UNSUPPORTED;
+  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_E_UNSUPPORTED;
+  if ((a->scale_kind != NVFP4_SCALE_1D16 && a->scale_kind != NVFP4_SCALE_2D16) ||
+      (b->scale_kind != NVFP4_SCALE_1D16 && b->scale_kind != NVFP4_SCALE_2D16))
+    return NVFP4_E_UNSUPPORTED;
+  if (ldc < b->rows) return NVFP4_E_LD;
+  if (!aligned16(a->codes) || !aligned16(b->codes) || !aligned16(c)) return NVFP4_E_ALIGN;
+  if (workspace && !aligned16(workspace)) return NVFP4_E_ALIGN;
+  if (a->rows > ((int64_t)1 << 31) || b->rows > ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+  return NVFP4_OK;
+}
+
+GemmArgs gemm_args(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc) {
+  GemmArgs g;
+  g.a_codes = a->codes;
+  g.a_scales = a->scales;
+  g.a_S = a->global_scale;
+  g.b_codes = b->codes;
+  g.b_scales = b->scales;
+  g.b_S = b->global_scale;
+  g.c = c;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->cols;
+  g.ldc = ldc;
+  g.a_kind = a->scale_kind;
+  g.b_kind = b->scale_kind;
+  g.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
+  return g;
+}
+
 OutArgs out_args(const nvfp4_quant_output &o, int amax_mode) {
   OutArgs a;
   a.codes = o.out.codes;
   a.scales = o.out.scales;
   a.S_out = o.out.global_scale;
   a.amax_out = o.out.amax;
+  a.amax_in = (o.flags & NVFP4_AMAX_GIVEN) ? o.out.amax : nullptr;
   a.sr_seed = o.sr_seed;
   a.amax_mode = amax_mode;
   a.pad = 0;
@@ -191,14 +230,18 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
   aa.partials = partials;
   aa.mask_rows = mask_rows;
   aa.mask_cols = mask_cols;
-  bool plain = false, rc = false, rr = false;
+  bool plain = false, rc = false, rr = false;  // maxima the amax pass must produce
   for (int i = 0; i < n_outs; ++i) {
+    if (outs[i].flags & NVFP4_AMAX_GIVEN) continue;
     plain |= p[i].amax_mode == AM_PLAIN;
     rc |= p[i].amax_mode == AM_RHT_COL;
     rr |= p[i].amax_mode == AM_RHT_ROW;
   }
-  hipError_t e = launch_amax(aa, plain, rc, rr, nparts, s);
-  if (e != hipSuccess) return NVFP4_E_HIP;
+  hipError_t e = hipSuccess;
+  if (plain || rc || rr) {
+    e = launch_amax(aa, plain, rc, rr, nparts, s);
+    if (e != hipSuccess) return NVFP4_E_HIP;
+  }
   qa.nparts = nparts;
   e = launch_quantize(qa, p0.geom, p0.rht, p0.sr, p1.geom, p1.rht, p1.sr, s, &supported);
   if (!supported) return NVFP4_E_UNSUPPORTED;
@@ -234,34 +277,27 @@ size_t nvfp4_gemm_workspace_bytes(void) {
 
 int nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int32_t c_dtype, int64_t ldc, void *workspace,
                size_t workspace_bytes, void *stream) {
-  if (!a || !b || !c) return NVFP4_E_NULL;
-  if (!a->codes || !a->scales || !a->global_scale || !b->codes || !b->scales || !b->global_scale) return NVFP4_E_NULL;
-  if (a->rows <= 0 || b->rows <= 0 || a->cols <= 0 || (a->rows % 16) || (b->rows % 16) || (a->cols % 16))
-    return NVFP4_E_SHAPE;
-  if (a->cols != b->cols) return NVFP4_E_UNSUPPORTED;
-  if (c_dtype != NVFP4_F32 && c_dtype != NVFP4_BF16) return NVFP4_E_UNSUPPORTED;
-  if ((a->scale_kind != NVFP4_SCALE_1D16 && a->scale_kind != NVFP4_SCALE_2D16) ||
-      (b->scale_kind != NVFP4_SCALE_1D16 && b->scale_kind != NVFP4_SCALE_2D16))
-    return NVFP4_E_UNSUPPORTED;
-  if (ldc < b->rows) return NVFP4_E_LD;
-  if (!aligned16(a->codes) || !aligned16(b->codes) || !aligned16(c)) return NVFP4_E_ALIGN;
-  if (workspace && !aligned16(workspace)) return NVFP4_E_ALIGN;
-  if (a->rows > ((int64_t)1 << 31) || b->rows > ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
-  GemmArgs g;
-  g.a_codes = a->codes;
-  g.a_scales = a->scales;
-  g.a_S = a->global_scale;
-  g.b_codes = b->codes;
-  g.b_scales = b->scales;
-  g.b_S = b->global_scale;
-  g.c = c;
-  g.M = a->rows;
-  g.N = b->rows;
-  g.K = a->cols;
-  g.ldc = ldc;
-  g.a_kind = a->scale_kind;
-  g.b_kind = b->scale_kind;
-  g.c_bf16 = c_dtype == NVFP4_BF16 ? 1 : 0;
+  const int st = gemm_check(a, b, c, c_dtype, ldc, workspace);
+  if (st != NVFP4_OK) return st;
+  GemmArgs g = gemm_args(a, b, c, c_dtype, ldc);
+  g.amax_plain = nullptr;
+  g.amax_rht = nullptr;
+  g.rht_mask = 0;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(launch_gemm(g, workspace, workspace_bytes, s), s);
+}
+
+int nvfp4_gemm_amax(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int64_t ldc, void *workspace,
+                    size_t workspace_bytes, float *amax_plain, float *amax_rht_col, uint64_t rht_seed, void *stream) {
+  if (!amax_plain && !amax_rht_col) return NVFP4_E_NULL;
+  if (((uintptr_t)amax_plain & 3u) || ((uintptr_t)amax_rht_col & 3u)) return NVFP4_E_ALIGN;
+  // the validation of nvfp4_gemm, without enqueueing anything
+  const int st = gemm_check(a, b, c, NVFP4_BF16, ldc, workspace);
+  if (st != NVFP4_OK) return st;
+  GemmArgs g = gemm_args(a, b, c, NVFP4_BF16, ldc);
+  g.amax_plain = reinterpret_cast<unsigned int *>(amax_plain);
+  g.amax_rht = reinterpret_cast<unsigned int *>(amax_rht_col);
+  g.rht_mask = nvfp4_rht_sign_mask(rht_seed);
   hipStream_t s = (hipStream_t)stream;
   return finish(launch_gemm(g, workspace, workspace_bytes, s), s);
 }

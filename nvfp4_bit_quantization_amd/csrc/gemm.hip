@@ -53,6 +53,98 @@ __device__ __forceinline__ _Float16 scale_f16(uint32_t scales4, int blk) {
   return (_Float16)e4m3_value(b);
 }
 
+// ---------------------------------------------------------------------------
+// Producer-fused maxima of a bf16 output (nvfp4_gemm_amax): the per-tensor
+// maxima the quantisation of C needs, taken from the rounded outputs while
+// they are in registers, so that the quantiser need not read C for them.
+//   plain: max |c| over the stored bf16 values;
+//   RHT along rows: max |H16 D c| / 4 over the aligned 16-row groups (the
+//   transform a column-blocked quantisation of C applies; D from the mask).
+// The transform of a 32x32 accumulator block is one product Z = T C on the
+// bf16 MFMA (two 16-deep K-steps), T block-diagonal with two copies of H16 D.
+// The accumulator layout (lane half h holds rows (r >> 2) 8 + 4h + (r & 3))
+// serves directly as the K order of the B operand: K-step s takes r = 8s ..
+// 8s + 7, i.e. the rows rho(k) = (k & 3) | (h << 2) | ((k >> 2) << 3) of
+// group s, k = 8h + kk, and T's columns are permuted to match.  Products with
+// +-1 are exact; the sums are fp32.  Each wave folds its maxima with one
+// device-scope atomic maximum per tensor (bit patterns of non-negative floats
+// order like the values).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// A operand of K-step s: lane l supplies row i = l % 32 of Z and k = 8 (l/32) + kk
+__device__ __forceinline__ bf16x8v rht_rows_operand(uint32_t mask, uint32_t s, uint32_t lane) {
+  const uint32_t i = lane & 31u, hh = lane >> 5;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t kk = 2 * q + e;
+      const uint32_t rho = (kk & 3u) | (hh << 2) | ((kk >> 2) << 3);  // row of the 16-row group
+      const uint32_t neg = (__builtin_popcount((i & 15u) & rho) + ((mask >> rho) & 1u)) & 1u;
+      const uint32_t v = (i >> 4) == s ? (neg ? 0xBF80u : 0x3F80u) : 0u;
+      pair |= v << (16 * e);
+    }
+    w[q] = pair;
+  }
+  return __builtin_bit_cast(bf16x8v, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+struct FusedMax {
+  bf16x8v t0, t1;     // the transform's A operands (K-steps 0 and 1)
+  uint32_t plain;     // max of |c| as bf16 magnitude bits
+  float rht;          // max |H16 D c| (unnormalised)
+};
+
+__device__ __forceinline__ void fused_max_init(FusedMax &f, const GemmArgs &g, uint32_t lane) {
+  f.plain = 0;
+  f.rht = 0.0f;
+  if (g.amax_rht) {
+    f.t0 = rht_rows_operand(g.rht_mask, 0, lane);
+    f.t1 = rht_rows_operand(g.rht_mask, 1, lane);
+  }
+}
+
+// fold one 32x32 block's 16 rounded values (bf16 bit patterns) of this lane
+__device__ __forceinline__ void fused_max_block(FusedMax &f, const GemmArgs &g, const uint32_t hb[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f.plain = max(f.plain, hb[r] & 0x7FFFu);
+  if (g.amax_rht) {
+    const bf16x8v b0 = __builtin_bit_cast(
+        bf16x8v, make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)));
+    const bf16x8v b1 = __builtin_bit_cast(bf16x8v, make_uint4(hb[8] | (hb[9] << 16), hb[10] | (hb[11] << 16),
+                                                              hb[12] | (hb[13] << 16), hb[14] | (hb[15] << 16)));
+    float16v z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.t0, b0, z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.t1, b1, z, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f.rht = fmaxf(f.rht, fabsf(z[r]));
+  }
+}
+
+__device__ __forceinline__ void fused_max_flush(const FusedMax &f, const GemmArgs &g) {
+  uint32_t mp = f.plain;
+  float mr = f.rht;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mp = max(mp, (uint32_t)__shfl_xor((int)mp, off, 64));
+    mr = fmaxf(mr, __shfl_xor(mr, off, 64));
+  }
+  if ((threadIdx.x & 63u) == 0) {
+    if (g.amax_plain) atomicMax(g.amax_plain, mp << 16);
+    if (g.amax_rht) atomicMax(g.amax_rht, __float_as_uint(mr * 0.25f));  // the exact 1/4 of the transform
+  }
+}
+
 template <int TM, int TN>
 struct GemmTile {
   static constexpr int BM = 64 * TM;
@@ -202,28 +294,33 @@ __global__ __launch_bounds__(kGThreads) void gemm_generic_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: C = acc / (S_A S_B)
+  // epilogue: C = acc / (S_A S_B); outputs past M or N are zero (zero
+  // operands), so they do not change the fused maxima
   const float inv = 1.0f / (*g.a_S * *g.b_S);
+  const bool fused = g.c_bf16 && (g.amax_plain || g.amax_rht);
+  FusedMax fm;
+  if (fused) fused_max_init(fm, g, lane);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t n = n0 + wn * (TN * 32) + j * 32 + lrow;
+      uint32_t hb[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+        const float v = acc[i][j][r] * inv;
+        hb[r] = bf16_rne_bits(v);
         if (m < g.M && n < g.N) {
-          const float v = acc[i][j][r] * inv;
-          if (g.c_bf16) {
-            const uint32_t u = __float_as_uint(v);
-            const uint16_t h = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);  // nearest-even
-            reinterpret_cast<uint16_t *>(g.c)[m * g.ldc + n] = h;
-          } else {
+          if (g.c_bf16)
+            reinterpret_cast<uint16_t *>(g.c)[m * g.ldc + n] = (uint16_t)hb[r];
+          else
             reinterpret_cast<float *>(g.c)[m * g.ldc + n] = v;
-          }
         }
       }
+      if (fused) fused_max_block(fm, g, hb);
     }
+  if (fused) fused_max_flush(fm, g);
 }
 
 // ===========================================================================
@@ -517,17 +614,24 @@ __device__ __forceinline__ void fast_store_c(const GemmArgs &g, int64_t m0, int6
   if (g.c_bf16) {
     uint16_t *ct = reinterpret_cast<uint16_t *>(g.c) + m0 * g.ldc + n0;
     asm volatile("" : "+s"(ct));  // keep the address arithmetic in the epilogue
+    const bool fused = g.amax_plain || g.amax_rht;
+    FusedMax fm;
+    if (fused) fused_max_init(fm, g, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hb[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
           const uint32_t n = wn * 128 + j * 32 + lr;
-          const uint32_t u = __float_as_uint(acc[i][j][r] * inv);
-          ct[m * ldc + n] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+          hb[r] = bf16_rne_bits(acc[i][j][r] * inv);
+          ct[m * ldc + n] = (uint16_t)hb[r];
         }
+        if (fused) fused_max_block(fm, g, hb);
+      }
+    if (fused) fused_max_flush(fm, g);
   } else {
     float *ct = reinterpret_cast<float *>(g.c) + m0 * g.ldc + n0;
     asm volatile("" : "+s"(ct));  // keep the address arithmetic in the epilogue

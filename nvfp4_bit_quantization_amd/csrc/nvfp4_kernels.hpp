@@ -36,6 +36,7 @@ struct OutArgs {
   uint8_t *scales;
   float *S_out;
   float *amax_out;
+  const float *amax_in;  // the output's maximum when given by the caller, else null (partials are reduced)
   uint64_t sr_seed;
   int amax_mode;
   int pad;
@@ -79,6 +80,11 @@ struct GemmArgs {
   int64_t M, N, K, ldc;
   int a_kind, b_kind;  // 0 = 1D scales, 1 = 2D scales
   int c_bf16;
+  // producer-fused maxima of the bf16 output (null: not wanted); bit patterns
+  // of non-negative floats, combined with atomic maxima
+  unsigned int *amax_plain;
+  unsigned int *amax_rht;
+  uint32_t rht_mask;  // RHT sign mask of the 16-row groups (amax_rht)
 };
 
 // MXFP4 (OCP MX v1.0): 32-element blocks with an E8M0 scale, no per-tensor scale

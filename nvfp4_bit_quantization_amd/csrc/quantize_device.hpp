@@ -352,8 +352,8 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
 }
 
 // Global scale of each output from the nparts partial maxima of its amax mode
-// (written by the amax pass), and the table r(c) = S / E4M3(c) of element
-// factors (0 for the zero scale).
+// (written by the amax pass) or from the maximum the caller gave, and the
+// table r(c) = S / E4M3(c) of element factors (0 for the zero scale).
 template <int NOUT>
 __device__ __forceinline__ void quant_setup(const QuantArgs &a, uint32_t nparts, float s_S[2],
                                             float s_lut[2][128]) {
@@ -363,7 +363,11 @@ __device__ __forceinline__ void quant_setup(const QuantArgs &a, uint32_t nparts,
   for (int o = 0; o < NOUT; ++o) {
     const float *part = a.partials + a.o[o].amax_mode * kMaxParts;
     float m = 0.0f;
-    for (uint32_t p = threadIdx.x; p < nparts; p += kQThreads) m = fmaxf(m, part[p]);
+    if (a.o[o].amax_in) {  // given by the caller (producer-fused)
+      if (threadIdx.x == 0) m = *a.o[o].amax_in;
+    } else {
+      for (uint32_t p = threadIdx.x; p < nparts; p += kQThreads) m = fmaxf(m, part[p]);
+    }
     m = wave_max(m);
     if (lane == 0) s_red[w] = m;
     __syncthreads();

@@ -57,8 +57,8 @@ def _tensor(rows, cols, kind, codes=FAKE):
     return nv.nvfp4_tensor(codes, FAKE, FAKE, FAKE, rows, cols, kind, 0)
 
 
-def _out(layout, rows, cols, kind, rounding=0, rht=0, reserved=0, codes=FAKE):
-    return nv.nvfp4_quant_output(layout, rounding, rht, reserved, 1, 2, _tensor(rows, cols, kind, codes))
+def _out(layout, rows, cols, kind, rounding=0, rht=0, flags=0, codes=FAKE):
+    return nv.nvfp4_quant_output(layout, rounding, rht, flags, 1, 2, _tensor(rows, cols, kind, codes))
 
 
 def _q(L, outs, x=FAKE, rows=64, cols=32, ld=32, ws=FAKE, wsb=None):
@@ -83,7 +83,7 @@ def test_quantize_argument_validation(L):
     assert _q(L, [_out(nv.TWO_D, 64, 32, nv.SCALE_2D16, rht=1)]) == -5  # RHT with 2D
     assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, rounding=7)]) == -5
     assert _q(L, [_out(9, 64, 32, nv.SCALE_1D16)]) == -5
-    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, reserved=1)]) == -5
+    assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, flags=2)]) == -5     # unknown flag
     assert _q(L, [_out(nv.ROW_1D, 32, 64, nv.SCALE_1D16)]) == -2        # descriptor shape mismatch
     assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_2D16)]) == -2        # wrong scale kind
     assert _q(L, [_out(nv.ROW_1D, 64, 32, nv.SCALE_1D16, codes=0)]) == -1
@@ -116,6 +116,13 @@ def test_dequantize_and_gemm_validation(L):
                         None) == -2
     ws = ctypes.c_void_p(FAKE + 8)                                                         # misaligned workspace
     assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 48, ws, 1 << 20, None) == -4
+    # producer-fused maxima: at least one target, 4-byte aligned, plus the GEMM's own checks
+    am = ctypes.c_void_p(FAKE)
+    assert L.nvfp4_gemm_amax(ctypes.byref(a), ctypes.byref(b), c, 48, None, 0, None, None, 0, None) == -1
+    assert L.nvfp4_gemm_amax(ctypes.byref(a), ctypes.byref(b), c, 48, None, 0, ctypes.c_void_p(FAKE + 2), None, 0,
+                             None) == -4
+    assert L.nvfp4_gemm_amax(ctypes.byref(a), ctypes.byref(bk), c, 48, None, 0, am, am, 0, None) == -5
+    assert L.nvfp4_gemm_amax(ctypes.byref(a), ctypes.byref(b), c, 40, None, 0, am, None, 0, None) == -3
     assert L.nvfp4_codec_selftest(3, None, None, None, 0, None) == -5
     assert L.nvfp4_codec_selftest(0, None, None, None, -1, None) == -2
     assert L.nvfp4_codec_selftest(0, None, None, None, 5, None) == -1

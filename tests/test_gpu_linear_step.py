@@ -59,8 +59,10 @@ def check_gemm(qa, qb, c, what, dt):
     assert err <= 1e-3, (what, err)
 
 
-def run_step(nv, T):
-    say("linear step", T, "tokens")
+def run_step(nv, T, fused=False):
+    """fused: the H and dH GEMMs produce the maxima of their outputs'
+    quantisations (nvfp4_gemm_amax), which then skip their amax pass."""
+    say("linear step", T, "tokens", "fused amax" if fused else "")
     d = syn.linear_step_16384(T, HID, FFN)
     dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in d.items()}
     S = nv.QuantSpec.of
@@ -77,14 +79,32 @@ def run_step(nv, T):
     gws = nv.new_gemm_workspace()
     qX = nv.quantize(dev["X"], sX)
     qW1 = nv.quantize(dev["W1"], sW)
-    H = nv.gemm(qX[0], qW1[0], "bf16", workspace=gws)             # H = X W1^T   [T][FFN]
-    qH = nv.quantize(H, sX)
+    if fused:
+        H = torch.empty((T, FFN), dtype=torch.bfloat16, device="cuda")
+        qH = [nv.empty_qtensor(T, FFN, nv.SCALE_1D16), nv.empty_qtensor(FFN, T, nv.SCALE_1D16, rht=1)]
+        for q in qH:
+            q.amax.zero_()
+        nv.nvfp4_gemm_amax(qX[0], qW1[0], H, qH[0].amax, qH[1].amax, 4321, workspace=gws)
+        sH = [S("row", amax_given=True), S("col", "rtn", True, 0, 4321, amax_given=True)]
+        nv.nvfp4_quantize(H, sH, qH, nv.new_workspace())
+    else:
+        H = nv.gemm(qX[0], qW1[0], "bf16", workspace=gws)         # H = X W1^T   [T][FFN]
+        qH = nv.quantize(H, sX)
     qW2 = nv.quantize(dev["W2"], sW)
     Y = nv.gemm(qH[0], qW2[0], "bf16", workspace=gws)             # Y = H W2^T   [T][HID]
     say("backward")
     qdY = nv.quantize(dev["dY"], sdY)
-    dH = nv.gemm(qdY[0], qW2[1], "bf16", workspace=gws)           # dH = dY W2   [T][FFN]
-    qdH = nv.quantize(dH, sdH)
+    if fused:
+        dH = torch.empty((T, FFN), dtype=torch.bfloat16, device="cuda")
+        qdH = [nv.empty_qtensor(T, FFN, nv.SCALE_1D16), nv.empty_qtensor(FFN, T, nv.SCALE_1D16, rht=1)]
+        for q in qdH:
+            q.amax.zero_()
+        nv.nvfp4_gemm_amax(qdY[0], qW2[1], dH, qdH[0].amax, qdH[1].amax, 4321, workspace=gws)
+        sdHf = [S("row", "sr", False, 1236, amax_given=True), S("col", "sr", True, 1237, 4321, amax_given=True)]
+        nv.nvfp4_quantize(dH, sdHf, qdH, nv.new_workspace())
+    else:
+        dH = nv.gemm(qdY[0], qW2[1], "bf16", workspace=gws)       # dH = dY W2   [T][FFN]
+        qdH = nv.quantize(dH, sdH)
     dX = nv.gemm(qdH[0], qW1[1], "bf16", workspace=gws)           # dX = dH W1   [T][HID]
     dW2 = nv.gemm(qdY[1], qH[1], "f32", workspace=gws)            # dW2 = dY^T H [HID][FFN]
     dW1 = nv.gemm(qdH[1], qX[1], "f32", workspace=gws)            # dW1 = dH^T X [FFN][HID]
@@ -123,3 +143,7 @@ def test_linear_step_stagewise(nv):
 
 def test_linear_step_16384_full(nv):
     run_step(nv, 16384)
+
+
+def test_linear_step_fused_amax(nv):
+    run_step(nv, 512, fused=True)
