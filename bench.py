@@ -201,18 +201,27 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
     sX = [S("row"), S("col", "rtn", True, 0, 4321)]
     sW = [S("2d"), S("2d_t")]
     sdY = [S("row", "sr", False, 1234), S("col", "sr", True, 1235, 4321)]
-    sdH = [S("row", "sr", False, 1236), S("col", "sr", True, 1237, 4321)]
+    # H and dH are GEMM outputs: their GEMMs produce the maxima of both of
+    # their quantisations (producer-fused amax), so those calls skip the amax pass
+    sH = [S("row", amax_given=True), S("col", "rtn", True, 0, 4321, amax_given=True)]
+    sdH = [S("row", "sr", False, 1236, amax_given=True), S("col", "sr", True, 1237, 4321, amax_given=True)]
+    amax4 = torch.zeros(4, dtype=f32, device="cuda")
+    qH[0].amax, qH[1].amax, qdH[0].amax, qdH[1].amax = amax4[0:1], amax4[1:2], amax4[2:3], amax4[3:4]
     g = 2.0 * tokens * ffn * hidden
+
+    def fprop_h():
+        amax4.zero_()
+        nv.nvfp4_gemm_amax(qX[0], qW1[0], H, qH[0].amax, qH[1].amax, 4321, gws)
 
     def step(t):
         t.run("q_X", lambda: nv.nvfp4_quantize(X, sX, qX, ws))
         t.run("q_W1", lambda: nv.nvfp4_quantize(W1, sW, qW1, ws))
-        t.run("fprop_H", lambda: nv.nvfp4_gemm(qX[0], qW1[0], H, gws))
-        t.run("q_H", lambda: nv.nvfp4_quantize(H, sX, qH, ws))
+        t.run("fprop_H", fprop_h)
+        t.run("q_H", lambda: nv.nvfp4_quantize(H, sH, qH, ws))
         t.run("q_W2", lambda: nv.nvfp4_quantize(W2, sW, qW2, ws))
         t.run("fprop_Y", lambda: nv.nvfp4_gemm(qH[0], qW2[0], Y, gws))
         t.run("q_dY", lambda: nv.nvfp4_quantize(dY, sdY, qdY, ws))
-        t.run("dgrad_dH", lambda: nv.nvfp4_gemm(qdY[0], qW2[1], dH, gws))
+        t.run("dgrad_dH", lambda: nv.nvfp4_gemm_amax(qdY[0], qW2[1], dH, qdH[0].amax, qdH[1].amax, 4321, gws))
         t.run("q_dH", lambda: nv.nvfp4_quantize(dH, sdH, qdH, ws))
         t.run("dgrad_dX", lambda: nv.nvfp4_gemm(qdH[0], qW1[1], dX, gws))
         t.run("wgrad_dW2", lambda: nv.nvfp4_gemm(qdY[1], qH[1], dW2, gws))
@@ -229,7 +238,8 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
         "wgrad_dW1": dict(kind="gemm", flops=g)}
     return step, dict(flops=6 * g, calls=calls, dominant="wgrad_dW2",
                       config=dict(workload="linear_step_16384", tokens=tokens, hidden=hidden, ffn=ffn,
-                                  step="Fprop H,Y; Dgrad dH,dX; Wgrad dW2,dW1; 6 quantise calls"))
+                                  step="Fprop H,Y; Dgrad dH,dX; Wgrad dW2,dW1; 6 quantise calls; "
+                                       "H and dH maxima fused into their GEMMs"))
 
 
 def setup_mx_wgrad(nv, syn, tokens=8192, hidden=5120):
