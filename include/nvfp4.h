@@ -35,7 +35,8 @@
  *     reaches that point, and inputs must not change before then;
  *   - arguments are validated on the host before anything is enqueued; on an
  *     error nothing is written and a negative status is returned;
- *   - inputs must be finite (NaN/Inf give unspecified outputs).
+ *   - inputs must be finite (NaN/Inf give unspecified outputs); with the RHT,
+ *     |x| < 2^124, so that the binary32 sums of 16 terms stay finite.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

@@ -143,6 +143,27 @@ def test_edge_cases(nv):
     check(nv, syn.f32_to_bf16_bits(x), [dict(layout="row"), dict(layout="col")], "grid")
 
 
+def test_extreme_dynamic_range(nv):
+    """Blocks that hold values near the bf16 maximum next to bf16 subnormals:
+    the scaled subnormal elements underflow in binary32 (y = v * r_b rounds
+    to a subnormal or to a signed zero), which the stochastic-rounding encoder
+    must see exactly as the oracle does (bit-exact, several seeds); the RHT
+    paths with inputs below 2^124, where the 16-term sums stay finite."""
+    rng = np.random.default_rng(21)
+    R, C = 64, 96
+    sub = rng.integers(1, 128, (R, C)).astype(np.uint16) | (rng.integers(0, 2, (R, C)).astype(np.uint16) << 15)
+    big = syn.f32_to_bf16_bits((rng.choice([-1, 1], (R, C)) * rng.uniform(1e37, 3.3e38, (R, C))).astype(np.float32))
+    x = np.where(rng.random((R, C)) < 0.1, big, sub).astype(np.uint16)
+    for seed in (1, 2, 3):
+        check(nv, x, [dict(layout="row", rounding="sr", sr_seed=seed),
+                      dict(layout="col", rounding="sr", sr_seed=seed + 10)], "extreme-sr")
+    check(nv, x, [dict(layout="2d_t", rounding="sr", sr_seed=4)], "extreme-sr-2dt")
+    lim = syn.f32_to_bf16_bits((rng.choice([-1, 1], (R, C)) * rng.uniform(1e30, 2.0e37, (R, C))).astype(np.float32))
+    xr = np.where(rng.random((R, C)) < 0.1, lim, sub).astype(np.uint16)
+    check(nv, xr, [dict(layout="col", rounding="sr", rht=True, sr_seed=5, rht_seed=6)], "extreme-rht-sr")
+    check(nv, xr, [dict(layout="row", rht=True, rht_seed=7)], "extreme-rht-rtn")
+
+
 def test_strided_input(nv):
     bits = syn.activation(64, 96, seed=5)
     big = np.zeros((64, 128), np.uint16)
