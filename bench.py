@@ -234,7 +234,7 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
         "q_W2": dict(kind="quantize", bytes=2 * ffn * hidden + 2 * (ffn * hidden // 2 + ffn * hidden // 256)),
         "fprop_Y": dict(kind="gemm", flops=g), "q_dY": dict(kind="quantize", bytes=qbytes(tokens, hidden, 2)),
         "dgrad_dH": dict(kind="gemm", flops=g), "q_dH": dict(kind="quantize", bytes=qbytes(tokens, ffn, 2)),
-        "dgrad_dX": dict(kind="gemm", flops=g), "wgrad_dW2": dict(kind="gemm", flops=g),
+        "dgrad_dX": dict(kind="gemm", flops=g), "wgrad_dW2": dict(kind="gemm", flops=g, M=hidden, N=ffn, K=tokens),
         "wgrad_dW1": dict(kind="gemm", flops=g)}
     return step, dict(flops=6 * g, calls=calls, dominant="wgrad_dW2",
                       config=dict(workload="linear_step_16384", tokens=tokens, hidden=hidden, ffn=ffn,
@@ -259,7 +259,7 @@ def setup_mx_wgrad(nv, syn, tokens=8192, hidden=5120):
     info = dict(flops=flops, calls={
         "quantize_dY": dict(kind="quantize", bytes=mxbytes),
         "quantize_X": dict(kind="quantize", bytes=mxbytes),
-        "gemm_wgrad": dict(kind="gemm", flops=flops, peak=MFMA_FP4_PEAK_TFLOPS)},
+        "gemm_wgrad": dict(kind="gemm", flops=flops, peak=MFMA_FP4_PEAK_TFLOPS, M=hidden, N=hidden, K=tokens)},
         dominant="gemm_wgrad", kernel="mx_gemm_fast_kernel",
         sources=("mxfp4.hip", "gemm_device.hpp", "nvfp4_kernels.hpp"),
         dtype="mxfp4 operands (E2M1, E8M0 per 32); fp32 quantise math; fp4 MFMA with block scales, fp32 accumulate",
@@ -276,6 +276,27 @@ WORKLOADS = {"wgrad_8192x5120": setup_wgrad, "act_8192x5120": setup_act, "weight
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the workload
 # ---------------------------------------------------------------------------
+def library_gemm(M: int, N: int, K: int, reps: int = 30):
+    """torch.matmul (hipBLASLt) in bf16 on random [M][K] x [N][K]^T operands:
+    TFLOP/s and ms per call, HIP events around `reps` back-to-back calls."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(5):
+        a @ b.t()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        a @ b.t()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return dict(tflops=round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1), ms=round(ms, 4), shape="%dx%dx%d" % (M, N, K),
+                what="torch.matmul bf16 (hipBLASLt), random operands, A [M][K] x B[N][K]^T")
+
+
 def cpu_baseline(workload: str, syn):
     import oracle
     try:
@@ -351,6 +372,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wgrad_8192x5120", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-library-gemm", action="store_true",
+                    help="skip timing torch.matmul in bf16 on the dominant GEMM's shape")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run a plain device copy of N MiB (for scaling the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -439,6 +462,14 @@ def main():
         quant = dict(gbs=round(qb / (qms * 1e-3) / 1e9, 1), frac_hbm=round(qb / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      bytes=qb, ms=round(qms, 4))
 
+    # context for the GEMM roofline: the library's dense bf16 GEMM (torch.matmul,
+    # hipBLASLt) on random operands of the dominant GEMM's shape, after the timed
+    # region; the NVFP4 GEMM expands 4-bit operands to fp16 and runs at the same
+    # MFMA rate, so this is the practical ceiling on this GPU's clocks
+    lib_gemm = None
+    if dc["kind"] == "gemm" and "M" in dc and not args.no_library_gemm:
+        lib_gemm = library_gemm(dc["M"], dc["N"], dc["K"])
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a sample)")
@@ -452,6 +483,8 @@ def main():
         "data": "synthetic",
         "config": info["config"], "quantize": quant, "calls": parts, "roofline": roof, "cpu_baseline": cpu,
     }
+    if lib_gemm is not None:
+        out["library_bf16_gemm"] = lib_gemm
     print(json.dumps(out), flush=True)
 
 
