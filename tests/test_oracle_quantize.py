@@ -3,8 +3,9 @@
 Each check is fixed by mathematics or by the page rather than by the oracle's
 own formulas: nearest-grid optimality of every RTN element (brute force over the
 block's 16 candidate values), SR neighbours, the block-max statement of
-paragraph 2 of the NVFP4 pretraining news page (zubnet.ai: the FP32 overlay
-puts at least 6.25 % of each block -- its maximum -- at near-FP8 precision),
+paragraph 2 of the NVFP4 pretraining news page (zubnet.ai: with the per-tensor
+FP32 scale on top, one element in sixteen -- the block maximum -- keeps close
+to FP8 precision),
 exact round trips of representable inputs, the transpose identities of 2D
 block scaling (paragraph 2: forward and backward see the same quantised
 weights), orthogonality of the Hadamard step, and the GEMM against a plain
