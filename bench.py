@@ -236,7 +236,8 @@ def setup_linear(nv, syn, tokens=16384, hidden=5120, ffn=20480):
         "dgrad_dH": dict(kind="gemm", flops=g), "q_dH": dict(kind="quantize", bytes=qbytes(tokens, ffn, 2)),
         "dgrad_dX": dict(kind="gemm", flops=g), "wgrad_dW2": dict(kind="gemm", flops=g, M=hidden, N=ffn, K=tokens),
         "wgrad_dW1": dict(kind="gemm", flops=g)}
-    return step, dict(flops=6 * g, calls=calls, dominant="wgrad_dW2",
+    # dW2 (1600 256x256 tiles: 6.25 rounds on 256 CUs) runs as stream-K
+    return step, dict(flops=6 * g, calls=calls, dominant="wgrad_dW2", kernel="gemm_streamk_kernel",
                       config=dict(workload="linear_step_16384", tokens=tokens, hidden=hidden, ffn=ffn,
                                   step="Fprop H,Y; Dgrad dH,dX; Wgrad dW2,dW1; 6 quantise calls; "
                                        "H and dH maxima fused into their GEMMs"))
