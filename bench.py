@@ -298,7 +298,24 @@ def library_gemm(M: int, N: int, K: int, reps: int = 30):
                 what="torch.matmul bf16 (hipBLASLt), random operands, A [M][K] x B[N][K]^T")
 
 
+def one_thread(fn) -> float:
+    """Wall time of fn() with the oracle's parallel loops and the BLAS on one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    n = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            fn()
+            return time.perf_counter() - t0
+    finally:
+        oracle.set_threads(n)
+
+
 def cpu_baseline(workload: str, syn):
+    """The oracle timed on the host: on all threads (``value``) and on one
+    (``value_1thread``; its GEMM timed on a row sample and scaled)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -315,11 +332,15 @@ def cpu_baseline(workload: str, syn):
         oracle.gemm_f64(qa, qb)
         t2 = time.perf_counter()
         flops = 2.0 * 5120 * 5120 * 8192
+        tq1 = one_thread(lambda: (oracle.quantize(dy, "col", "sr", True, 1234, 1234),
+                                  oracle.quantize(xx, "col", "rtn", True, 0, 1234)))
+        tg1 = 8 * one_thread(lambda: oracle.gemm_f64(qa, qb, rows_a=np.arange(640)))
         return dict(value=flops / (t2 - t0) / 1e12, unit="TFLOP/s", cores=max(qthreads, blas_threads),
-                    kind="oracle",
+                    kind="oracle", value_1thread=flops / (tq1 + tg1) / 1e12,
                     sample="the whole Wgrad workload (dY, X 8192x5120): C oracle quantise (col+RHT, SR/RTN; "
-                           "%d threads, %.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s)"
-                           % (qthreads, t1 - t0, blas_threads, t2 - t1))
+                           "%d threads, %.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s); "
+                           "1 thread: quantise %.2f s, GEMM 8 x the time of 640 rows of C, %.2f s"
+                           % (qthreads, t1 - t0, blas_threads, t2 - t1, tq1, tg1))
     if workload == "mx_wgrad_8192x5120":
         dy, xx = syn.wgrad_8192x5120()
         t0 = time.perf_counter()
@@ -329,11 +350,13 @@ def cpu_baseline(workload: str, syn):
         oracle.mx_gemm_f64(qa, qb)
         t2 = time.perf_counter()
         flops = 2.0 * 5120 * 5120 * 8192
+        tq1 = one_thread(lambda: (oracle.mx_quantize(dy, "col"), oracle.mx_quantize(xx, "col")))
         return dict(value=flops / (t2 - t0) / 1e12, unit="TFLOP/s", cores=max(qthreads, blas_threads),
-                    kind="oracle",
+                    kind="oracle", value_1thread=flops / (tq1 + (t2 - t1) * blas_threads) / 1e12,
                     sample="the whole MXFP4 Wgrad workload (dY, X 8192x5120): C oracle MX quantise (%d threads, "
-                           "%.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s)"
-                           % (qthreads, t1 - t0, blas_threads, t2 - t1))
+                           "%.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s); 1 thread: "
+                           "quantise %.2f s, GEMM estimated as the BLAS time x its threads"
+                           % (qthreads, t1 - t0, blas_threads, t2 - t1, tq1))
     if workload in ("act_8192x5120", "weight_5120x20480", "tiny_256"):
         if workload == "act_8192x5120":
             bits, specs = syn.act_8192x5120(2048, 5120), ["row", "col"]
@@ -348,21 +371,29 @@ def cpu_baseline(workload: str, syn):
         for s in specs:
             oracle.quantize(bits, s)
         dt = time.perf_counter() - t0
+        dt1 = one_thread(lambda: [oracle.quantize(bits, s) for s in specs])
         return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=qthreads, kind="oracle",
-                    sample="%s quantise of a %dx%d slice (C oracle, %d threads, %.2f s)" % (
-                        "+".join(specs), bits.shape[0], bits.shape[1], qthreads, dt))
+                    value_1thread=nbytes / dt1 / 1e9,
+                    sample="%s quantise of a %dx%d slice (C oracle, %d threads, %.2f s; 1 thread %.2f s)" % (
+                        "+".join(specs), bits.shape[0], bits.shape[1], qthreads, dt, dt1))
     # linear step: one Wgrad GEMM + its two quantisations on a 1/8 token slice
     tokens, hidden, ffn = 2048, 5120, 2560
     dy = syn.laplace(tokens, hidden, 504, 1e-3)
     h = syn.normal(tokens, ffn, 501)
+    def run():
+        qa = oracle.quantize(dy, "col", "sr", True, 1235, 4321)
+        qb = oracle.quantize(h, "col", "rtn", True, 0, 4321)
+        oracle.gemm_f64(qa, qb)
+
     t0 = time.perf_counter()
-    qa = oracle.quantize(dy, "col", "sr", True, 1235, 4321)
-    qb = oracle.quantize(h, "col", "rtn", True, 0, 4321)
-    oracle.gemm_f64(qa, qb)
+    run()
     dt = time.perf_counter() - t0
+    dt1 = one_thread(run)
     flops = 2.0 * hidden * ffn * tokens
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=max(qthreads, blas_threads), kind="oracle",
-                sample="dW2 slice: 2048 tokens, 5120x2560 Wgrad with both column quantisations (%.2f s)" % dt)
+                value_1thread=flops / dt1 / 1e12,
+                sample="dW2 slice: 2048 tokens, 5120x2560 Wgrad with both column quantisations (%.2f s; "
+                       "1 thread %.2f s)" % (dt, dt1))
 
 
 # ---------------------------------------------------------------------------

@@ -69,6 +69,7 @@ def _load():
     f32, f64 = ctypes.c_float, ctypes.c_double
     sig = {
         "oracle_threads": (i32, []),
+        "oracle_set_threads": (None, [i32]),
         "oracle_e2m1_value": (f64, [ctypes.c_uint8]),
         "oracle_e2m1_encode_rtn": (ctypes.c_uint8, [f32]),
         "oracle_e2m1_encode_sr": (ctypes.c_uint8, [f32, ctypes.c_uint16]),
@@ -115,6 +116,11 @@ def _ptr(a: np.ndarray):
 def threads() -> int:
     """Threads the oracle's parallel loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Set the threads of the oracle's parallel loops (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def e2m1_value(code: int) -> float:

@@ -69,6 +69,17 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Set the threads of the parallel loops (n >= 1; no effect without OpenMP).
+ * Results do not depend on it: every loop writes disjoint outputs, and the
+ * one reduction is a maximum. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 static float bf16_bits_to_float(uint16_t h) {
   uint32_t u = (uint32_t)h << 16; /* bf16 is the top half of a binary32 */
   float f;
