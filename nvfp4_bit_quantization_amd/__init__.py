@@ -8,10 +8,11 @@ HIP kernels.  Importing this package fails loudly when the library has not
 been built (``python -m nvfp4_bit_quantization_amd.build``); there is no CPU
 fallback.
 
-Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1 elements
-in 16-element blocks, E4M3 block scales, an FP32 per-tensor scale, 1D blocks
-for activations/gradients and 16x16 blocks for weights, stochastic rounding for
-gradients, 16x16 random Hadamard transforms on Wgrad inputs.
+Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- blocks of 16
+E2M1 values with an E4M3 scale each, an FP32 scale per tensor, 1D blocks for
+activations/gradients and 16x16 blocks for weights, stochastic rounding for
+gradients, a 16-point randomised Hadamard transform on the weight-gradient
+inputs.
 """
 from __future__ import annotations
 

@@ -2,9 +2,10 @@
 // block-scale codec, the E2M1 element encoders, Philox4x32-10 and the 16-point
 // Hadamard butterfly.
 //
-// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1 elements
-// in 16-element blocks, E4M3 block scales, FP32 per-tensor scale, stochastic
-// rounding for gradients, 16x16 random Hadamard transforms on Wgrad inputs.
+// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- blocks of 16
+// E2M1 values with an E4M3 scale each, an FP32 scale per tensor, stochastic
+// rounding for gradients, a 16-point randomised Hadamard transform on the
+// weight-gradient inputs.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -3,11 +3,11 @@
 // per-tile maxima, the block-scale and element encoders, one output of one
 // micro-tile, and the global-scale setup.
 //
-// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1
-// elements in 16-element blocks with an E4M3 scale per block and an FP32
-// per-tensor scale; 1D blocks for activations/gradients, 16x16 blocks for
-// weights; stochastic rounding for gradients; 16x16 random Hadamard transforms
-// with random signs on Wgrad inputs.
+// Method: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- blocks of
+// 16 E2M1 values share one E4M3 scale, under one FP32 scale per tensor; 1D
+// blocks for activations/gradients, 16x16 blocks for weights; stochastic
+// rounding for gradients; a 16-point Hadamard transform with a random +-1
+// sign vector on the weight-gradient inputs.
 //
 // Work decomposition.  A workgroup (4 waves) owns a 128 x 256 tile of the
 // bf16 input.  Each lane owns a 16-row x 8-column micro-tile, loaded as 16

@@ -11,9 +11,10 @@ it against on small shapes).
 
 Method source: the NVFP4 pretraining news page (zubnet.ai,
 "nvidia-nvfp4-paper-4-bit-pretrain-hits-fp8-parity-12b-10t-tokens", en/pt/fr/hi
-versions), paragraph 2: E2M1 elements in 16-element blocks with E4M3 block
-scales and an FP32 per-tensor scale; 16x16 RHT with random signs on Wgrad
-inputs; 2D block scaling for weights; stochastic rounding for gradients.
+versions), paragraph 2: blocks of 16 E2M1 values, each with an E4M3 scale,
+under one FP32 scale per tensor; a 16x16 RHT with random signs on the
+weight-gradient inputs; 16x16 scale blocks for weights; stochastic rounding for
+gradients.
 
 MXFP4 (the earlier microscaling format the page compares NVFP4 with, paragraph
 3) follows the OCP Microscaling Formats (MX) specification v1.0, since the page

@@ -8,11 +8,12 @@
  * with the HIP path.
  *
  * Source of the method: "NVIDIA NVFP4 paper: 4-bit pretrain hits FP8 parity"
- * (zubnet.ai news page, en/pt/fr/hi), paragraph 2 ("four stabilization
- * techniques" / "the format itself"): E2M1 elements in 16-element blocks, an
- * E4M3 scale per block, an FP32 per-tensor scale on top; 16x16 Random
- * Hadamard Transforms with random +/-1 signs on Wgrad inputs; 2D block scaling
- * for weights; stochastic rounding on gradients only.  The page gives no
+ * (zubnet.ai news page, en/pt/fr/hi), paragraph 2 (the stabilising
+ * techniques and the number format): blocks of 16 E2M1 values with an E4M3
+ * scale each, under one FP32 scale per tensor; a 16x16 randomised Hadamard
+ * transform (random +/-1 signs) on the weight-gradient inputs; 16x16 scale
+ * blocks for weights; stochastic rounding for gradients and for nothing else.
+ * The page gives no
  * formulas; the arithmetic convention below (global scale 448*6/amax, block
  * scale E4M3(amax_b/6 * S), elements scaled onto the E2M1 grid
  * {0,.5,1,1.5,2,3,4,6}) is the fixed convention of this project, and every

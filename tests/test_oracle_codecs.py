@@ -5,8 +5,8 @@ scipy's Hadamard matrix, rocRAND's open-source Philox engine), published
 known-answer vectors, closed forms and statistical bounds.
 
 Method source: NVFP4 pretraining news page (zubnet.ai), paragraph 2 -- E2M1
-elements, E4M3 block scales, 16x16 random Hadamard transforms with random
-signs, stochastic rounding for gradients.
+values, E4M3 block scales, a 16-point Hadamard transform with a random sign
+vector, stochastic rounding for gradients.
 """
 import math
 import os
