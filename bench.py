@@ -56,11 +56,37 @@ def qbytes(rows, cols, outs=1):
     return 2 * n + outs * (n // 2 + n // 16)
 
 
+def code_only(src: str) -> str:
+    """C/HIP source without comments and whitespace (string literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_hash(*names):
+    """Hash of the code (comments and whitespace excluded) of the named
+    sources: counter profiles taken on other code are not reused."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "nvfp4_bit_quantization_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "nvfp4_bit_quantization_amd", "csrc", n)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
