@@ -176,6 +176,49 @@ def test_strided_input(nv):
     assert_bit_exact(gpu_q_as_dict(outs[1]), run_oracle(bits, dict(layout="col")), "strided-col")
 
 
+@pytest.mark.parametrize("specs", [
+    [dict(layout="col", rounding="sr", rht=True, sr_seed=21, rht_seed=22)],
+    [dict(layout="row", rounding="sr", rht=True, sr_seed=23, rht_seed=24)],
+    [dict(layout="2d"), dict(layout="2d_t")],
+    [dict(layout="row", rounding="sr", sr_seed=25), dict(layout="col", rounding="sr", rht=True, sr_seed=26,
+                                                        rht_seed=27)],
+], ids=["col-rht-sr", "row-rht-sr", "2d-pair", "row-sr+col-rht-sr"])
+def test_strided_input_every_kind(nv, specs):
+    """A padded input (row stride 312 elements for 272 columns): every output
+    kind reads only the first 272 columns of each row."""
+    bits = syn.laplace(144, 272, seed=31, scale=1e-3)
+    big = np.full((144, 312), 0x7F00, np.uint16)  # padding: a huge bf16 value that would change every maximum
+    big[:, :272] = bits
+    say("strided", specs)
+    x = dev_bf16(big)[:, :272]
+    outs = nv.quantize(x, [nv.QuantSpec.of(**d) for d in specs])
+    torch.cuda.synchronize()
+    for q, d in zip(outs, specs):
+        g, o = gpu_q_as_dict(q), run_oracle(bits, d)
+        if d.get("rht"):
+            assert_rht_tolerance(g, o, "strided %s" % d)
+        else:
+            assert_bit_exact(g, o, "strided %s" % d)
+
+
+@pytest.mark.parametrize("layout", ["row", "2d_t"])
+def test_dequantize_into_strided_output(nv, layout):
+    """Dequantise into a padded fp32 output (row stride cols + 12): the values
+    match the oracle bit for bit and the padding is not written."""
+    bits = syn.activation(144, 272, seed=98)
+    say("dequant strided", layout)
+    _, outs = run_gpu(nv, bits, [dict(layout=layout)])
+    q = outs[0]
+    big = torch.full((q.rows, q.cols + 12), -3.0, dtype=torch.float32, device="cuda")
+    nv.nvfp4_dequantize(q, big[:, :q.cols])
+    torch.cuda.synchronize()
+    yb = host(big)
+    o = run_oracle(bits, dict(layout=layout))
+    assert np.array_equal(np.ascontiguousarray(yb[:, :q.cols]).view(np.uint32),
+                          oracle.dequantize(o).view(np.uint32))
+    assert np.all(yb[:, q.cols:] == -3.0)
+
+
 def test_guard_bands_and_determinism(nv):
     """Canary bytes around every output stay untouched; repeated runs are identical."""
     bits = syn.laplace(144, 272, seed=8)
