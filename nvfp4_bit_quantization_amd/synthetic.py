@@ -96,3 +96,18 @@ def wgrad_8192x5120(tokens: int = 8192, hidden: int = HIDDEN):
 def linear_step_16384(tokens: int = 16384, hidden: int = HIDDEN, ffn: int = FFN):
     return dict(X=normal(tokens, hidden, 501), W1=normal(ffn, hidden, 502, std=0.02),
                 W2=normal(hidden, ffn, 503, std=0.02), dY=laplace(tokens, hidden, 504, 1e-3))
+
+
+def normal_device(rows: int, cols: int, seed: int, peak_at=None, peak: float = 64.0):
+    """N(0,1) bf16 tensor drawn on the GPU by torch's seeded generator, for
+    tensors too large to draw on the host (the maximum-size test); the value
+    `peak` is planted at `peak_at` = (row, col) so that the tensor maximum is
+    known.  Both sides read these bytes: the kernels on the device, the oracle
+    from slices copied to the host."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn((rows, cols), dtype=torch.bfloat16, device="cuda", generator=g)
+    if peak_at is not None:
+        x[peak_at[0], peak_at[1]] = peak
+    return x

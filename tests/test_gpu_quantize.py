@@ -253,6 +253,41 @@ def test_guard_bands_and_determinism(nv):
         assert host(sc)[0] == -7.0 and host(sc)[2] == -7.0 and host(am)[0] == -7.0 and host(am)[2] == -7.0
 
 
+def test_maximum_size_row_and_col(nv):
+    """The largest tensor the ABI accepts for 1D outputs: 524272 x 65536 bf16
+    (64 GiB), (rows/16) * cols = 2^31 - 65536 blocks, so block indices and
+    stochastic-rounding counters reach their upper range.  One read gives the
+    row output (RTN) and the column output (RHT, RTN).  The value 64 is planted
+    in the last element, so the tensor maximum (plain and in the RHT domain) is
+    the maximum of any slice holding it; the oracle quantises such slices (the
+    last 16 rows for the row output, the last 16 columns for the column
+    output), so the global scale is the oracle's own."""
+    R, C = 524272, 65536
+    if torch.cuda.get_device_properties(0).total_memory < 160 * 2**30:
+        pytest.skip("needs about 110 GB of device memory")
+    say("max size: draw", R, C)
+    x = syn.normal_device(R, C, seed=77, peak_at=(R - 1, C - 1))
+    specs = [nv.QuantSpec.of("row"), nv.QuantSpec.of("col", "rtn", True, 0, 4321)]
+    say("max size: quantize")
+    outs = nv.quantize(x, specs)
+    torch.cuda.synchronize()
+    rows_bits = host(x[R - 16:].contiguous().view(torch.int16)).view(np.uint16)
+    cols_bits = host(x[:, C - 16:].contiguous().view(torch.int16)).view(np.uint16)
+    del x
+    say("max size: oracle slices")
+    o_row = run_oracle(rows_bits, dict(layout="row"))
+    o_col = run_oracle(cols_bits, dict(layout="col", rht=True, rht_seed=4321))
+    g_row = dict(codes=host(outs[0].codes[R - 16:]), scales=host(outs[0].scales[R - 16:]),
+                 S=np.float32(host(outs[0].global_scale)[0]), amax=np.float32(host(outs[0].amax)[0]))
+    g_col = dict(codes=host(outs[1].codes[C - 16:]), scales=host(outs[1].scales[C - 16:]),
+                 S=np.float32(host(outs[1].global_scale)[0]), amax=np.float32(host(outs[1].amax)[0]))
+    del outs
+    torch.cuda.empty_cache()
+    assert float(o_row["amax"]) == 64.0
+    assert_bit_exact(g_row, o_row, "max-size row")
+    assert_rht_tolerance(g_col, o_col, "max-size col RHT")
+
+
 # ------------------------------------------------------------- full sizes
 def test_act_8192x5120_row_and_col(nv):
     """Activation 8192x5120: row 1D + column 1D from one read, RTN (bit-exact)."""
