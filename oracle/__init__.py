@@ -81,6 +81,7 @@ def _load():
         "oracle_rht_sign_mask": (ctypes.c_uint16, [u64]),
         "oracle_rht16_f64": (None, [P, ctypes.c_uint16, P]),
         "oracle_quantize": (i32, [P, i64, i64, i64, i32, i32, i32, u64, u64, P, P, P, P]),
+        "oracle_quantize_at": (i32, [P, i64, i64, i64, i32, i32, i32, u64, u64, u64, P, P, P, P]),
         "oracle_dequantize": (i32, [P, P, i64, i64, i32, f32, P]),
         "oracle_decode_products": (i32, [P, P, i64, i64, i32, P]),
         "oracle_gemm_f64": (i32, [P, P, i32, f32, P, P, i32, f32, i64, i64, i64, P]),
@@ -232,9 +233,12 @@ def scale_shape(rows: int, cols: int, layout: int):
     return orow, ocol // 16
 
 
-def quantize(x_bits: np.ndarray, layout="row", rounding="rtn", rht=False, sr_seed=0, rht_seed=0) -> Dict:
+def quantize(x_bits: np.ndarray, layout="row", rounding="rtn", rht=False, sr_seed=0, rht_seed=0,
+             block_offset=0) -> Dict:
     """Quantise a bf16 tensor given as uint16 bit patterns [R][C].
 
+    ``block_offset`` numbers the stochastic-rounding blocks of a slice of a
+    larger tensor as in the whole (the blocks before the slice in output order).
     Returns dict(codes [orow][ocol/2] uint8, scales uint8, S float32,
     amax float32, rows, cols, scale_kind)."""
     layout = LAYOUTS.get(layout, layout)
@@ -246,8 +250,8 @@ def quantize(x_bits: np.ndarray, layout="row", rounding="rtn", rht=False, sr_see
     scales = np.zeros(scale_shape(R, C, layout), dtype=np.uint8)
     S = np.zeros(1, dtype=np.float32)
     amax = np.zeros(1, dtype=np.float32)
-    rc = _load().oracle_quantize(_ptr(x_bits), R, C, C, layout, rounding, int(bool(rht)), sr_seed, rht_seed,
-                                 _ptr(codes), _ptr(scales), _ptr(S), _ptr(amax))
+    rc = _load().oracle_quantize_at(_ptr(x_bits), R, C, C, layout, rounding, int(bool(rht)), sr_seed, rht_seed,
+                                    int(block_offset), _ptr(codes), _ptr(scales), _ptr(S), _ptr(amax))
     if rc != 0:
         raise ValueError("oracle_quantize rejected the arguments (rc=%d)" % rc)
     kind = SCALE_2D16 if layout in (TWO_D, TWO_D_T) else SCALE_1D16

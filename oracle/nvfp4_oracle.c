@@ -275,9 +275,24 @@ static float v_at(const uint16_t *x, int64_t ld, int64_t r, int64_t c) {
   return bf16_bits_to_float(x[r * ld + c]);
 }
 
+int oracle_quantize_at(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int layout, int rounding, int rht,
+                       uint64_t sr_seed, uint64_t rht_seed, uint64_t block_offset, uint8_t *codes, uint8_t *scales,
+                       float *S_out, float *amax_out);
+
 int oracle_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int layout, int rounding, int rht,
                     uint64_t sr_seed, uint64_t rht_seed, uint8_t *codes, uint8_t *scales, float *S_out,
                     float *amax_out) {
+  return oracle_quantize_at(x, R, C, ld, layout, rounding, rht, sr_seed, rht_seed, 0, codes, scales, S_out,
+                            amax_out);
+}
+
+/* As oracle_quantize, for a slice of a larger tensor: the stochastic-rounding
+ * block index is block_offset + the slice's own block index (block_offset =
+ * the blocks that precede the slice in output order, e.g. rows x cols/16 for
+ * a slice starting at that output row).  Everything else is unchanged. */
+int oracle_quantize_at(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int layout, int rounding, int rht,
+                       uint64_t sr_seed, uint64_t rht_seed, uint64_t block_offset, uint8_t *codes, uint8_t *scales,
+                       float *S_out, float *amax_out) {
   if (R <= 0 || C <= 0 || (R % 16) || (C % 16) || ld < C) return -1;
   if (layout < OR_ROW_1D || layout > OR_2D_T) return -1;
   if (rounding != OR_RTN && rounding != OR_SR) return -1;
@@ -361,7 +376,7 @@ int oracle_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int lay
           } else {
             /* block order: row-major 1D block index of the working
              * orientation (2D uses its row blocks too) */
-            uint64_t b = (uint64_t)r * (uint64_t)nbc + (uint64_t)bc;
+            uint64_t b = block_offset + (uint64_t)r * (uint64_t)nbc + (uint64_t)bc;
             code = oracle_e2m1_encode_sr(y, oracle_sr_uniform(sr_seed, b, j));
           }
           /* store the code */

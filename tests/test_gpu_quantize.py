@@ -257,7 +257,9 @@ def test_maximum_size_row_and_col(nv):
     """The largest tensor the ABI accepts for 1D outputs: 524272 x 65536 bf16
     (64 GiB), (rows/16) * cols = 2^31 - 65536 blocks, so block indices and
     stochastic-rounding counters reach their upper range.  One read gives the
-    row output (RTN) and the column output (RHT, RTN).  The value 64 is planted
+    row output and the column output (RHT), both with stochastic rounding.  The
+    oracle numbers the slices' blocks as in the whole tensor (block_offset).
+    The value 64 is planted
     in the last element, so the tensor maximum (plain and in the RHT domain) is
     the maximum of any slice holding it; the oracle quantises such slices (the
     last 16 rows for the row output, the last 16 columns for the column
@@ -267,7 +269,7 @@ def test_maximum_size_row_and_col(nv):
         pytest.skip("needs about 110 GB of device memory")
     say("max size: draw", R, C)
     x = syn.normal_device(R, C, seed=77, peak_at=(R - 1, C - 1))
-    specs = [nv.QuantSpec.of("row"), nv.QuantSpec.of("col", "rtn", True, 0, 4321)]
+    specs = [nv.QuantSpec.of("row", "sr", False, 91), nv.QuantSpec.of("col", "sr", True, 92, 4321)]
     say("max size: quantize")
     outs = nv.quantize(x, specs)
     torch.cuda.synchronize()
@@ -275,8 +277,8 @@ def test_maximum_size_row_and_col(nv):
     cols_bits = host(x[:, C - 16:].contiguous().view(torch.int16)).view(np.uint16)
     del x
     say("max size: oracle slices")
-    o_row = run_oracle(rows_bits, dict(layout="row"))
-    o_col = run_oracle(cols_bits, dict(layout="col", rht=True, rht_seed=4321))
+    o_row = oracle.quantize(rows_bits, "row", "sr", False, 91, 0, block_offset=(R - 16) * (C // 16))
+    o_col = oracle.quantize(cols_bits, "col", "sr", True, 92, 4321, block_offset=(C - 16) * (R // 16))
     g_row = dict(codes=host(outs[0].codes[R - 16:]), scales=host(outs[0].scales[R - 16:]),
                  S=np.float32(host(outs[0].global_scale)[0]), amax=np.float32(host(outs[0].amax)[0]))
     g_col = dict(codes=host(outs[1].codes[C - 16:]), scales=host(outs[1].scales[C - 16:]),

@@ -378,3 +378,26 @@ def test_bf16_output_rounding():
     for d in (-1, 1):
         nb = oracle.bf16_bits_to_f32((bits + d).astype(np.uint16)).astype(np.float64)
         assert np.all(np.abs(nb - c) >= np.abs(cb - c))
+
+
+def test_block_offset_numbers_a_slice_as_in_the_whole():
+    """A slice quantised with block_offset = the blocks before it in output
+    order gives, under stochastic rounding, exactly that part of the whole
+    tensor's result (the slice holds the tensor maximum, so the global scale is
+    the same); a wrong offset gives different codes."""
+    x = syn.laplace(64, 96, seed=61, scale=1e-3)
+    big = syn.f32_to_bf16_bits(np.float32(0.05) * np.ones(1, np.float32))[0]  # larger than every Laplace(1e-3) draw
+    x[40, 37] = big
+    whole_row = oracle.quantize(x, "row", "sr", False, 71, 0)
+    part_row = oracle.quantize(x[32:48], "row", "sr", False, 71, 0, block_offset=32 * (96 // 16))
+    assert part_row["S"] == whole_row["S"]
+    assert np.array_equal(part_row["codes"], whole_row["codes"][32:48])
+    assert np.array_equal(part_row["scales"], whole_row["scales"][32:48])
+    wrong = oracle.quantize(x[32:48], "row", "sr", False, 71, 0)
+    assert not np.array_equal(wrong["codes"], whole_row["codes"][32:48])
+    whole_col = oracle.quantize(x, "col", "sr", True, 72, 73)
+    part_col = oracle.quantize(np.ascontiguousarray(x[:, 32:48]), "col", "sr", True, 72, 73,
+                               block_offset=32 * (64 // 16))
+    assert part_col["S"] == whole_col["S"]
+    assert np.array_equal(part_col["codes"], whole_col["codes"][32:48])
+    assert np.array_equal(part_col["scales"], whole_col["scales"][32:48])
