@@ -176,3 +176,43 @@ def test_streamk_matches_whole_tiles(nv, gws, shape, monkeypatch):
         err = rel_frobenius(host(c1)[rows], ref)
         say("stream-K vs oracle", err)
         assert err <= 1e-3
+
+
+def test_gemm_fast_path_at_its_offset_limit(nv):
+    """The largest operands the 256x256 fast path takes: M = N = 4096 and
+    K = 2097024, so K/2 * 4096 = 2^32 - 262144 bytes of codes per operand and
+    the 32-bit transfer offsets reach their top range (the transfers add them,
+    zero-extended, to a 64-bit base).  A 16x16 sample of C, spread over the
+    first and last rows and columns, against the oracle's binary64 GEMM on the
+    GPU's own operand rows."""
+    M = N = 4096
+    K = 2097024
+    if torch.cuda.get_device_properties(0).total_memory < 80 * 2**30:
+        pytest.skip("needs about 45 GB of device memory")
+    say("offset limit: draw and quantise", M, N, K)
+    xa = syn.normal_device(M, K, seed=81)
+    qa = nv.quantize(xa, [nv.QuantSpec.of("row")])[0]
+    del xa
+    xb = syn.normal_device(N, K, seed=82)
+    qb = nv.quantize(xb, [nv.QuantSpec.of("row")])[0]
+    del xb
+    torch.cuda.empty_cache()
+    say("offset limit: gemm")
+    c = nv.gemm(qa, qb, "f32")
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 1023, 2047, 2048, 3071, 3839, 3840, 4000, 4090, 4092, 4093, 4094, 4095])
+    cols = np.array([0, 7, 128, 255, 256, 1000, 2047, 2049, 3000, 3583, 3584, 3900, 4064, 4093, 4094, 4095])
+
+    def sub(q, idx):
+        return dict(codes=host(q.codes[torch.as_tensor(idx, device="cuda")]),
+                    scales=host(q.scales[torch.as_tensor(idx, device="cuda")]),
+                    S=np.float32(host(q.global_scale)[0]), rows=len(idx), cols=K, scale_kind=q.scale_kind)
+
+    say("offset limit: oracle sample")
+    ref = oracle.round_output(oracle.gemm_f64(sub(qa, rows), sub(qb, cols)), "f32")
+    got = host(c)[np.ix_(rows, cols)]
+    del qa, qb, c
+    torch.cuda.empty_cache()
+    err = rel_frobenius(got, ref)
+    say("offset limit rel err", err)
+    assert err <= 1e-3
