@@ -137,3 +137,41 @@ def test_mx_wgrad_8192x5120_sampled(nv):
     err = rel_frobenius(host(c)[rows], ref)
     say("mx wgrad sampled rel err", err)
     assert err <= 1e-5
+
+
+def test_mx_gemm_fast_path_at_its_offset_limit(nv):
+    """The largest operands the MX 256x256 fast path takes: M = N = 4096 and
+    K = 2096000 (M * K/2 + K just under 2^32), so its 32-bit transfer offsets
+    reach their top range.  A 16x16 sample of C over the first and last rows
+    and columns against the oracle on the GPU's own operand rows."""
+    M = N = 4096
+    K = 2096000
+    assert M * (K // 2) + K < 2 ** 32
+    if torch.cuda.get_device_properties(0).total_memory < 80 * 2**30:
+        pytest.skip("needs about 45 GB of device memory")
+    say("mx offset limit: draw and quantise", M, N, K)
+    xa = syn.normal_device(M, K, seed=83)
+    qa = nv.mx_quantize(xa, "row")
+    del xa
+    xb = syn.normal_device(N, K, seed=84)
+    qb = nv.mx_quantize(xb, "row")
+    del xb
+    torch.cuda.empty_cache()
+    say("mx offset limit: gemm")
+    c = nv.mx_gemm(qa, qb, "f32")
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 1023, 2047, 2048, 3071, 3839, 3840, 4000, 4090, 4092, 4093, 4094, 4095])
+    cols = np.array([0, 7, 128, 255, 256, 1000, 2047, 2049, 3000, 3583, 3584, 3900, 4064, 4093, 4094, 4095])
+
+    def sub(q, idx):
+        t = torch.as_tensor(idx, device="cuda")
+        return dict(codes=host(q.codes[t]), scales=host(q.scales[t]), rows=len(idx), cols=K)
+
+    say("mx offset limit: oracle sample")
+    ref = oracle.round_output(oracle.mx_gemm_f64(sub(qa, rows), sub(qb, cols)), "f32")
+    got = host(c)[np.ix_(rows, cols)]
+    del qa, qb, c
+    torch.cuda.empty_cache()
+    err = rel_frobenius(got, ref)
+    say("mx offset limit rel err", err)
+    assert err <= 1e-5
