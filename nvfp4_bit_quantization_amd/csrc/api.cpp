@@ -99,6 +99,8 @@ int gemm_check(const nvfp4_tensor *a, const nvfp4_tensor *b, const void *c, int3
   if (!aligned16(a->codes) || !aligned16(b->codes) || !aligned16(c)) return NVFP4_E_ALIGN;
   if (workspace && !aligned16(workspace)) return NVFP4_E_ALIGN;
   if (a->rows > ((int64_t)1 << 31) || b->rows > ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
+  // one workgroup per 256x256 tile of C: the grid size is a 32-bit count
+  if (((a->rows + 255) / 256) * ((b->rows + 255) / 256) >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
   return NVFP4_OK;
 }
 

@@ -116,6 +116,9 @@ def test_dequantize_and_gemm_validation(L):
                         None) == -2
     ws = ctypes.c_void_p(FAKE + 8)                                                         # misaligned workspace
     assert L.nvfp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 48, ws, 1 << 20, None) == -4
+    big = (1 << 31) - 16                                       # 2^46 tiles of C: more than the 32-bit grid holds
+    assert L.nvfp4_gemm(ctypes.byref(_tensor(big, 32, 0)), ctypes.byref(_tensor(big, 32, 0)), c, 0, big, None, 0,
+                        None) == -2
     # producer-fused maxima: at least one target, 4-byte aligned, plus the GEMM's own checks
     am = ctypes.c_void_p(FAKE)
     assert L.nvfp4_gemm_amax(ctypes.byref(a), ctypes.byref(b), c, 48, None, 0, None, None, 0, None) == -1
