@@ -76,6 +76,10 @@ PAIRS = [
     [dict(layout="row", rounding="sr", sr_seed=1236), dict(layout="col", rounding="sr", rht=True, sr_seed=1237,
                                                           rht_seed=4321)],
     [dict(layout="row", rht=True, rht_seed=3), dict(layout="col", rounding="sr", sr_seed=4)],
+    # the RHT on both outputs (each along its own blocked dimension, own sign vector)
+    [dict(layout="row", rht=True, rht_seed=5), dict(layout="col", rht=True, rht_seed=6)],
+    [dict(layout="col", rounding="sr", rht=True, sr_seed=7, rht_seed=8),
+     dict(layout="row", rounding="sr", rht=True, sr_seed=9, rht_seed=10)],
     [dict(layout="2d"), dict(layout="2d_t")],
     [dict(layout="2d", rounding="sr", sr_seed=21), dict(layout="2d_t", rounding="sr", sr_seed=21)],
 ]
