@@ -15,10 +15,13 @@ single-pass quantise of dY and X along tokens, GEMM on the block-scaled FP4
 MFMA; its roofline is against the FP4 matrix peak).
 
 Prints ONE JSON line.  ``value`` is whole-step throughput (GEMM flops of the
-step over the wall time per step, inputs resident in HBM); per-call times come
-from HIP events recorded on the stream the library launches on.  The
-``roofline`` object is for the dominant kernel; ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload.
+step over the wall time per step, inputs resident in HBM).  In the timed steps
+only the dominant call is bracketed by HIP events (on the stream the library
+launches on), which gives the roofline's kernel time; the other per-call times
+come from further steps after the timed region with every call bracketed, as
+each event pair adds GPU time to a step.  The ``roofline`` object is for the
+dominant kernel; ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -105,13 +108,19 @@ def read_traffic(kernel_tag: str, src_hash: str):
 
 
 class Timer:
-    """HIP events around library calls on the current stream."""
+    """HIP events around library calls on the current stream.  With `live`
+    given, only the calls named there are bracketed (the others just run):
+    every event pair adds a few microseconds of GPU time to a step."""
 
-    def __init__(self):
+    def __init__(self, live=None):
         self.marks = {}
+        self.live = live
 
     def run(self, name, fn):
         import torch
+        if self.live is not None and name not in self.live:
+            fn()
+            return
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
@@ -432,6 +441,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-library-gemm", action="store_true",
                     help="skip timing torch.matmul in bf16 on the dominant GEMM's shape")
+    ap.add_argument("--breakdown-steps", type=int, default=20,
+                    help="steps after the timed region with every call bracketed by events (per-call times)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run a plain device copy of N MiB (for scaling the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -465,7 +476,10 @@ def main():
     torch.cuda.synchronize()
     log("warmup done (%d steps)" % args.warmup)
 
-    t = Timer()
+    # timed region: only the dominant call is bracketed by events (its
+    # roofline time); the step's wall time gives `value`
+    dom = info["dominant"]
+    t = Timer(live={dom})
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -475,9 +489,18 @@ def main():
     ms_step = wall / args.steps * 1e3
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
 
+    # per-call breakdown, after the timed region: every call bracketed
+    tb = Timer()
+    for _ in range(args.breakdown_steps):
+        step(tb)
+    torch.cuda.synchronize()
+
+    def call_ms(name):
+        return t.ms(name) if name == dom else tb.ms(name)
+
     parts = {}
     for name, c in info["calls"].items():
-        ms = t.ms(name)
+        ms = call_ms(name)
         if c["kind"] == "gemm":
             tf = c["flops"] / (ms * 1e-3) / 1e12
             parts[name] = dict(ms=round(ms, 4), tflops=round(tf, 1),
@@ -486,7 +509,6 @@ def main():
             gbs = c["bytes"] / (ms * 1e-3) / 1e9
             parts[name] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
 
-    dom = info["dominant"]
     dc = info["calls"][dom]
     dms = t.ms(dom)
     if dc["kind"] == "gemm":
@@ -516,7 +538,7 @@ def main():
     quant = None
     if qcalls:
         qb = sum(info["calls"][n]["bytes"] for n in qcalls)
-        qms = sum(t.ms(n) for n in qcalls)
+        qms = sum(call_ms(n) for n in qcalls)
         quant = dict(gbs=round(qb / (qms * 1e-3) / 1e9, 1), frac_hbm=round(qb / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      bytes=qb, ms=round(qms, 4))
 
