@@ -164,7 +164,8 @@ int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream
  *              the fp32 partial sums of a split tile added in the workspace.  Without one (or if the runtime
  *              refuses the cooperative launch) every workgroup computes whole
  *              tiles.  The environment variable NVFP4_GEMM_DATA_PARALLEL
- *              forces whole tiles.  Calls that may run concurrently need
+ *              forces whole tiles, and so does a stream that is being
+ *              captured into a graph.  Calls that may run concurrently need
  *              separate workspaces.  The stream-K wait is bounded: if it ever
  *              times out, the word at byte offset 4096 of the workspace becomes
  *              non-zero and that call's output is invalid.

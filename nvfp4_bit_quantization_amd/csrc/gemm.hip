@@ -815,8 +815,16 @@ hipError_t launch_gemm(const GemmArgs &g, void *workspace, size_t workspace_byte
   // units idle.  (With fewer rounds the split tiles' pipeline refills and
   // partial sums cost more than the idle units of one short last round, which
   // also runs at a higher clock: measured on 5120x5120x8192.)
+  // a stream being captured into a graph gets whole tiles (the stream-K
+  // kernel's cooperative launch is not something to record in a graph)
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    capture = hipStreamCaptureStatusActive;  // unknown: take the path that needs no cooperative launch
+  }
   int dev = 0, cus = 0;
-  if (workspace && !getenv("NVFP4_GEMM_DATA_PARALLEL") && hipGetDevice(&dev) == hipSuccess &&
+  if (workspace && capture == hipStreamCaptureStatusNone && !getenv("NVFP4_GEMM_DATA_PARALLEL") &&
+      hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 &&
       cus <= kGemmMaxCUs && tiles > 2 * (int64_t)cus && workspace_bytes >= gemm_workspace_bytes(cus)) {
     const int64_t rounds = (tiles + cus - 1) / cus;

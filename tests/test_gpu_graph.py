@@ -77,3 +77,48 @@ def test_step_replays_from_a_graph(nv):
         torch.cuda.synchronize()
         for k, (t, r) in enumerate(zip(outs, ref)):
             assert torch.equal(t, r), "replay %d output %d differs from the eager step" % (i, k)
+
+
+def test_streamk_shape_captured_takes_whole_tiles(nv):
+    """A GEMM with a workspace on a shape that runs as stream-K when launched
+    eagerly (4352x8448, K = 1024: 4.3 rounds of tiles) is captured as whole
+    tiles; its replays equal an eager whole-tile launch bit for bit and the
+    eager stream-K result to fp32 accumulation-order level."""
+    M, N, K = 4352, 8448, 1024
+    qa = nv.quantize(dev_bf16(syn.normal(M, K, seed=61)), [nv.QuantSpec.of("row")])[0]
+    qb = nv.quantize(dev_bf16(syn.normal(N, K, seed=62)), [nv.QuantSpec.of("row")])[0]
+    gws = nv.new_gemm_workspace()
+    gws.zero_()
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    say("graph stream-K shape: eager")
+    nv.nvfp4_gemm(qa, qb, c, gws)
+    torch.cuda.synchronize()
+    c_sk = c.clone()
+    import os
+    os.environ["NVFP4_GEMM_DATA_PARALLEL"] = "1"
+    try:
+        nv.nvfp4_gemm(qa, qb, c, gws)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["NVFP4_GEMM_DATA_PARALLEL"]
+    c_dp = c.clone()
+    say("graph stream-K shape: capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.nvfp4_gemm(qa, qb, c, gws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.nvfp4_gemm(qa, qb, c, gws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        c.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c, c_dp), "replay %d differs from the eager whole-tile launch" % i
+    assert not nv.gemm_workspace_timed_out(gws)
+    rel = float((c - c_sk).norm() / c_sk.norm())
+    assert rel <= 1e-6, rel
