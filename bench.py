@@ -442,7 +442,7 @@ def main():
     ap.add_argument("--no-library-gemm", action="store_true",
                     help="skip timing torch.matmul in bf16 on the dominant GEMM's shape")
     ap.add_argument("--breakdown-steps", type=int, default=20,
-                    help="steps after the timed region with every call bracketed by events (per-call times)")
+                    help="steps (at least 1) after the timed region with every call bracketed by events (per-call times)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run a plain device copy of N MiB (for scaling the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -491,7 +491,7 @@ def main():
 
     # per-call breakdown, after the timed region: every call bracketed
     tb = Timer()
-    for _ in range(args.breakdown_steps):
+    for _ in range(max(1, args.breakdown_steps)):
         step(tb)
     torch.cuda.synchronize()
 
