@@ -47,6 +47,9 @@ CASES = [  # (M, N, K, a layout, b layout, out dtype)
     (512, 768, 384, "row", "2d", "bf16"),
     (768, 512, 1280, "2d", "row", "f32"),
     (1024, 1024, 2048, "col", "col", "f32"),
+    # both operands with 16x16 (weight) scales, fast path and direct kernel
+    (512, 512, 1024, "2d", "2d", "bf16"),
+    (304, 272, 576, "2d", "2d", "f32"),
 ]
 
 
