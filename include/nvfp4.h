@@ -36,7 +36,10 @@
  *   - arguments are validated on the host before anything is enqueued; on an
  *     error nothing is written and a negative status is returned;
  *   - inputs must be finite (NaN/Inf give unspecified outputs); with the RHT,
- *     |x| < 2^124, so that the binary32 sums of 16 terms stay finite.
+ *     |x| < 2^124, so that the binary32 sums of 16 terms stay finite;
+ *   - debugging: with the environment variable NVFP4_SYNC_CHECK=1 (read once
+ *     per process) every call also waits for its stream and returns
+ *     NVFP4_E_HIP if a kernel failed.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

@@ -98,3 +98,33 @@ def test_e2m1_sr_encoder(nv):
     want = oracle.e2m1_encode_sr(ys, us)
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, (ys[bad[:5]], us[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_sync_check_mode_in_a_child_process():
+    """NVFP4_SYNC_CHECK=1 (read once per process) makes every call wait for
+    its stream: the same quantise and GEMM calls succeed and give the same
+    codes and product as without it."""
+    import os
+    import subprocess
+    import sys
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    prog = (
+        "import sys, hashlib; sys.path.insert(0, %r)\n"
+        "import numpy as np, torch\n"
+        "import nvfp4_bit_quantization_amd as nv\n"
+        "from nvfp4_bit_quantization_amd import synthetic as syn\n"
+        "x = torch.from_numpy(syn.laplace(256, 512, seed=3).view(np.int16)).view(torch.bfloat16).cuda()\n"
+        "qa = nv.quantize(x, [nv.QuantSpec.of('row', 'sr', False, 5)])[0]\n"
+        "c = nv.gemm(qa, qa, 'f32')\n"
+        "torch.cuda.synchronize()\n"
+        "print(hashlib.sha256(qa.codes.cpu().numpy().tobytes() + c.cpu().numpy().tobytes()).hexdigest())\n"
+    ) % root
+    outs = []
+    for flag in ("0", "1"):
+        env = dict(os.environ, NVFP4_SYNC_CHECK=flag)
+        r = subprocess.run([sys.executable, "-c", prog], env=env, capture_output=True, text=True, timeout=240)
+        assert r.returncode == 0, r.stderr[-2000:]
+        outs.append(r.stdout.strip().splitlines()[-1])
+    assert outs[0] == outs[1]
