@@ -128,8 +128,76 @@ class Timer:
         e.record()
         self.marks.setdefault(name, []).append((s, e))
 
+    def times(self, name):
+        return [s.elapsed_time(e) for s, e in self.marks[name]]
+
     def ms(self, name):
-        return float(np.mean([s.elapsed_time(e) for s, e in self.marks[name]]))
+        return float(np.mean(self.times(name)))
+
+    def stats(self, name):
+        """mean, median, min and max (ms) of the bracketed calls of `name`."""
+        t = np.array(self.times(name))
+        return dict(ms=round(float(t.mean()), 4), ms_median=round(float(np.median(t)), 4),
+                    ms_min=round(float(t.min()), 4), ms_max=round(float(t.max()), 4), n=int(t.size))
+
+
+class GpuSampler:
+    """Samples, from a host thread while the timed steps run, the GPU's board
+    power (hwmon power1_input, with its cap power1_cap) and its current
+    graphics-clock DPM level (pp_dpm_sclk) from sysfs: plain file reads, no
+    GPU work.  Fields are None where the files are absent."""
+
+    def __init__(self, period_s=0.0005):
+        import glob
+        import threading
+        cards = sorted(d for d in glob.glob("/sys/class/drm/card*/device") if os.path.exists(d + "/pp_dpm_sclk"))
+        self.dev = cards[0] if len(cards) == 1 else None
+        hw = sorted(glob.glob(self.dev + "/hwmon/hwmon*")) if self.dev else []
+        self.hw = hw[0] if hw else None
+        self.period = period_s
+        self.power, self.sclk = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            if self.hw:
+                v = self._read(self.hw + "/power1_input")
+                if v and v.strip().isdigit():
+                    self.power.append(int(v) / 1e6)  # microwatts -> W
+            if self.dev:
+                v = self._read(self.dev + "/pp_dpm_sclk")
+                m = re.search(r"(\d+)\s*[Mm]hz\s*\*", v or "")
+                if m:
+                    self.sclk.append(int(m.group(1)))
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        cap = self._read(self.hw + "/power1_cap") if self.hw else None
+        out = dict(samples=len(self.power),
+                   power_w_mean=round(float(np.mean(self.power)), 1) if self.power else None,
+                   power_w_max=round(float(np.max(self.power)), 1) if self.power else None,
+                   power_cap_w=round(int(cap) / 1e6, 1) if cap and cap.strip().isdigit() else None,
+                   sclk_dpm_mhz=sorted(set(self.sclk)) if self.sclk else None,
+                   source="sysfs hwmon power1_input/power1_cap, pp_dpm_sclk (current DPM level), sampled "
+                          "every ~%.1f ms during the timed steps" % (self.period * 1e3))
+        return out
 
 
 # ---------------------------------------------------------------------------
@@ -333,6 +401,50 @@ def library_gemm(M: int, N: int, K: int, reps: int = 30):
                 what="torch.matmul bf16 (hipBLASLt), random operands, A [M][K] x B[N][K]^T")
 
 
+def host_info():
+    """The host the CPU baseline ran on: CPU model, threads this process may
+    use, and the BLAS numpy calls for the oracle's GEMM."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        threads = os.cpu_count()
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = "%s %s" % (b.get("name", "?"), b.get("version", ""))
+        try:
+            from threadpoolctl import threadpool_info
+            libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+            if libs:
+                blas += " (%s, %s threads)" % (libs[0].get("internal_api"), libs[0].get("num_threads"))
+        except Exception:  # pragma: no cover
+            pass
+    except Exception:  # pragma: no cover
+        pass
+    return dict(cpu_model=model, threads=threads, blas=blas.strip() if blas else None)
+
+
+def median_time(fn, reps: int = 5) -> float:
+    """Median wall time (s) of `reps` calls of fn after one untimed call."""
+    fn()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
 def one_thread(fn) -> float:
     """Wall time of fn() with the oracle's parallel loops and the BLAS on one thread."""
     import oracle
@@ -360,22 +472,22 @@ def cpu_baseline(workload: str, syn):
     qthreads = oracle.threads()
     if workload == "wgrad_8192x5120":
         dy, xx = syn.wgrad_8192x5120()
-        t0 = time.perf_counter()
         qa = oracle.quantize(dy, "col", "sr", True, 1234, 1234)
         qb = oracle.quantize(xx, "col", "rtn", True, 0, 1234)
-        t1 = time.perf_counter()
-        oracle.gemm_f64(qa, qb)
-        t2 = time.perf_counter()
+        tq = median_time(lambda: (oracle.quantize(dy, "col", "sr", True, 1234, 1234),
+                                  oracle.quantize(xx, "col", "rtn", True, 0, 1234)))
+        tg = median_time(lambda: oracle.gemm_f64(qa, qb))
         flops = 2.0 * 5120 * 5120 * 8192
         tq1 = one_thread(lambda: (oracle.quantize(dy, "col", "sr", True, 1234, 1234),
                                   oracle.quantize(xx, "col", "rtn", True, 0, 1234)))
         tg1 = 8 * one_thread(lambda: oracle.gemm_f64(qa, qb, rows_a=np.arange(640)))
-        return dict(value=flops / (t2 - t0) / 1e12, unit="TFLOP/s", cores=max(qthreads, blas_threads),
-                    kind="oracle", value_1thread=flops / (tq1 + tg1) / 1e12,
-                    sample="the whole Wgrad workload (dY, X 8192x5120): C oracle quantise (col+RHT, SR/RTN; "
-                           "%d threads, %.2f s) + binary64 GEMM 5120x5120x8192 (BLAS, %d threads, %.2f s); "
-                           "1 thread: quantise %.2f s, GEMM 8 x the time of 640 rows of C, %.2f s"
-                           % (qthreads, t1 - t0, blas_threads, t2 - t1, tq1, tg1))
+        return dict(value=flops / (tq + tg) / 1e12, unit="TFLOP/s", cores=max(qthreads, blas_threads),
+                    kind="oracle", value_1thread=flops / (tq1 + tg1) / 1e12, host=host_info(),
+                    sample="the whole Wgrad workload (dY, X 8192x5120), medians of 5 runs after one warm-up: "
+                           "C oracle quantise (col+RHT, SR/RTN; %d threads, %.2f s) + binary64 GEMM "
+                           "5120x5120x8192 (BLAS, %d threads, %.2f s); 1 thread, one run: quantise %.2f s, "
+                           "GEMM 8 x the time of 640 rows of C, %.2f s"
+                           % (qthreads, tq, blas_threads, tg, tq1, tg1))
     if workload == "mx_wgrad_8192x5120":
         dy, xx = syn.wgrad_8192x5120()
         t0 = time.perf_counter()
@@ -441,6 +553,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-library-gemm", action="store_true",
                     help="skip timing torch.matmul in bf16 on the dominant GEMM's shape")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run steps back to back for this long before the counted warm-up (clock ramp)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps after the timed region with a 512 MiB write before each (caches flushed)")
     ap.add_argument("--breakdown-steps", type=int, default=20,
                     help="steps (at least 1) after the timed region with every call bracketed by events (per-call times)")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -470,22 +586,36 @@ def main():
     step, info = WORKLOADS[args.workload](nv, syn)
     torch.cuda.synchronize()
 
+    # Settle: the GPU leaves its idle clock state only after some
+    # milliseconds of work, so a short run would time the ramp rather than
+    # the kernels (measured: 5 + 20 steps of the Wgrad step gave the GEMM
+    # 398-400 us per call where 10 + 100 steps on the same GPU gave 360 us).
+    # Steps run back to back for --settle-ms before the counted warm-up
+    # steps; nothing about them is timed or reported.
+    settle = Timer(live=set())
+    n_settle, t_set = 0, time.perf_counter()
+    while (time.perf_counter() - t_set) * 1e3 < args.settle_ms:
+        for _ in range(4):
+            step(settle)
+        n_settle += 4
+        torch.cuda.synchronize()
     warm = Timer()
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
-    log("warmup done (%d steps)" % args.warmup)
+    log("settle %d steps, warmup done (%d steps)" % (n_settle, args.warmup))
 
     # timed region: only the dominant call is bracketed by events (its
     # roofline time); the step's wall time gives `value`
     dom = info["dominant"]
     t = Timer(live={dom})
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(t)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with GpuSampler() as sampler:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(t)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_step))
 
@@ -495,19 +625,34 @@ def main():
         step(tb)
     torch.cuda.synchronize()
 
+    # cold variant: a 512 MiB write before every step evicts L2 and the
+    # 256 MB MALL, so each call starts with its inputs in HBM only
+    tc = Timer()
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for k in range(args.cold_steps):
+            flush.fill_(k & 0xFF)
+            step(tc)
+        torch.cuda.synchronize()
+        del flush
+
     def call_ms(name):
         return t.ms(name) if name == dom else tb.ms(name)
 
-    parts = {}
-    for name, c in info["calls"].items():
-        ms = call_ms(name)
+    def rate(c, ms):
         if c["kind"] == "gemm":
             tf = c["flops"] / (ms * 1e-3) / 1e12
-            parts[name] = dict(ms=round(ms, 4), tflops=round(tf, 1),
-                               frac_mfma=round(tf / c.get("peak", MFMA_F16_PEAK_TFLOPS), 4))
-        else:
-            gbs = c["bytes"] / (ms * 1e-3) / 1e9
-            parts[name] = dict(ms=round(ms, 4), gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+            return dict(tflops=round(tf, 1), frac_mfma=round(tf / c.get("peak", MFMA_F16_PEAK_TFLOPS), 4))
+        gbs = c["bytes"] / (ms * 1e-3) / 1e9
+        return dict(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+
+    parts, cold = {}, {}
+    for name, c in info["calls"].items():
+        st = t.stats(name) if name == dom else tb.stats(name)
+        parts[name] = dict(st, **rate(c, st["ms"]))
+        if args.cold_steps > 0:
+            cs = tc.stats(name)
+            cold[name] = dict(ms_median=cs["ms_median"], ms_min=cs["ms_min"], **rate(c, cs["ms_median"]))
 
     dc = info["calls"][dom]
     dms = t.ms(dom)
@@ -519,14 +664,18 @@ def main():
         traffic = read_traffic("gemm_" + args.workload, src)
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=traffic,
-                    kernel=info.get("kernel", "gemm_fast_kernel<4,4>"), ms=round(dms, 4), source_hash=src)
+                    kernel=info.get("kernel", "gemm_fast_kernel<4,4>"), ms=round(dms, 4),
+                    ms_median=parts[dom]["ms_median"], ms_min=parts[dom]["ms_min"],
+                    frac_at_median=round(dc["flops"] / (parts[dom]["ms_median"] * 1e-3) / 1e12 / peak, 4),
+                    source_hash=src)
     else:
         achieved = dc["bytes"] / (dms * 1e-3) / 1e9
         src = source_hash("quantize.hip", "quantize_device.hpp", "nvfp4_device.hpp", "nvfp4_kernels.hpp")
         traffic = read_traffic("quantize_" + args.workload, src)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel="amax+quantize pass",
-                    ms=round(dms, 4), source_hash=src)
+                    ms=round(dms, 4), ms_median=parts[dom]["ms_median"], ms_min=parts[dom]["ms_min"],
+                    source_hash=src)
 
     if info["flops"] > 0:
         value = info["flops"] / (ms_step * 1e-3) / 1e12
@@ -562,6 +711,7 @@ def main():
         "dtype": info.get("dtype", "nvfp4 operands; fp32 quantise math; fp16 MFMA, fp32 accumulate"),
         "data": "synthetic",
         "config": info["config"], "quantize": quant, "calls": parts, "roofline": roof, "cpu_baseline": cpu,
+        "cold": cold or None, "gpu_power": sampler.summary(), "settle_steps": n_settle,
     }
     if lib_gemm is not None:
         out["library_bf16_gemm"] = lib_gemm

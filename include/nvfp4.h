@@ -163,15 +163,18 @@ int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream
  *              round would leave more than a tenth of the compute units idle
  *              run as stream-K: whole tiles for the full rounds, then the
  *              remaining tiles' K-tiles spread evenly over one
- *              persistent workgroup per compute unit (a cooperative launch),
- *              the fp32 partial sums of a split tile added in the workspace.  Without one (or if the runtime
- *              refuses the cooperative launch) every workgroup computes whole
+ *              persistent workgroup per compute unit (the kernel's LDS use
+ *              admits one per CU, so on an otherwise idle GPU all are
+ *              resident), the fp32 partial sums of a split tile added in the
+ *              workspace.  Without one every workgroup computes whole
  *              tiles.  The environment variable NVFP4_GEMM_DATA_PARALLEL
  *              forces whole tiles, and so does a stream that is being
  *              captured into a graph.  Calls that may run concurrently need
  *              separate workspaces.  The stream-K wait is bounded: if it ever
  *              times out, the word at byte offset 4096 of the workspace becomes
- *              non-zero and that call's output is invalid.
+ *              non-zero and stays so, that call's output is invalid, and the
+ *              workspace must be zero-filled again before it is used again
+ *              (a late partial's flag may still be raised).
  * Operands are expanded exactly to fp16 in registers and multiplied on MFMA
  * with fp32 accumulation; the per-tensor scales are applied in the epilogue.
  */
@@ -206,7 +209,11 @@ int nvfp4_gemm_amax(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, int64
 size_t nvfp4_gemm_workspace_bytes(void);
 
 /* Host: the 16-bit RHT sign mask for a seed (bit j set => d_j = -1):
- * the low 16 bits of word 0 of Philox4x32-10(key = seed, counter = (0,0,1,0)). */
+ * the low 16 bits of word 0 of Philox4x32-10(key = seed, counter = (0,0,1,0)).
+ * Defines: page paragraph 2 (the random +/-1 signs of the 16-point randomised
+ * Hadamard transform); the counter and the bits taken are this library's
+ * convention.  One mask serves every 16-group of a tensor and both operands
+ * of a weight-gradient GEMM, so that the transforms cancel in the product. */
 uint16_t nvfp4_rht_sign_mask(uint64_t rht_seed);
 
 /* Host: a static description of a status code. */

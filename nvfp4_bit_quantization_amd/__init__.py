@@ -113,6 +113,21 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context under which the conveniences allocate: the stream the library
+    will launch on.  torch's caching allocator then hands a freed block (the
+    temporary quantise workspace) to later allocations on that same stream
+    only, i.e. after the kernels that use it; memory taken on another stream
+    could be reused while those kernels still run."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
+
+
 # ---------------------------------------------------------------------------
 # quantised tensors held in torch device memory
 # ---------------------------------------------------------------------------
@@ -253,8 +268,15 @@ def new_gemm_workspace(device="cuda"):
 
 
 def gemm_workspace_timed_out(workspace) -> bool:
-    """True if a stream-K call on this workspace hit its wait limit."""
+    """True if a stream-K call on this workspace hit its wait limit (the
+    outputs of that call are invalid; reset_gemm_workspace before reuse)."""
     return bool(workspace[4096:4100].view(__import__("torch").int32).item() != 0)
+
+
+def reset_gemm_workspace(workspace):
+    """Zero-fill a GEMM workspace again (needed after a timed-out call)."""
+    workspace.zero_()
+    return workspace
 
 
 def nvfp4_workspace_bytes() -> int:
@@ -280,26 +302,30 @@ def nvfp4_codec_selftest(which: int, x, u16, out, stream=None):
 # conveniences (allocation + one call)
 # ---------------------------------------------------------------------------
 def quantize(x, specs: Sequence[QuantSpec], workspace=None, stream=None) -> List[QTensor]:
-    """Allocate the outputs for `specs` and quantise x into them."""
-    if workspace is None:
-        workspace = new_workspace(x.device)
-    outs = []
-    for s in specs:
-        r, c, k = output_shape(x.shape[0], x.shape[1], s.layout)
-        outs.append(empty_qtensor(r, c, k, x.device, rht=int(s.rht)))
+    """Allocate the outputs for `specs` (and, if none is given, a workspace)
+    on the stream the call runs on, and quantise x into them."""
+    with _on_stream(stream):
+        if workspace is None:
+            workspace = new_workspace(x.device)
+        outs = []
+        for s in specs:
+            r, c, k = output_shape(x.shape[0], x.shape[1], s.layout)
+            outs.append(empty_qtensor(r, c, k, x.device, rht=int(s.rht)))
     return nvfp4_quantize(x, specs, outs, workspace, stream)
 
 
 def dequantize(q: QTensor, stream=None):
     import torch
-    y = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
+    with _on_stream(stream):
+        y = torch.empty((q.rows, q.cols), dtype=torch.float32, device=q.codes.device)
     return nvfp4_dequantize(q, y, stream)
 
 
 def gemm(a: QTensor, b: QTensor, out_dtype="f32", workspace=None, stream=None):
     import torch
     dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
-    c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
+    with _on_stream(stream):
+        c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
     return nvfp4_gemm(a, b, c, workspace, stream)
 
 
@@ -361,11 +387,14 @@ def mx_quantize(x, layout="row", stream=None) -> MXTensor:
     """Allocate the output and MXFP4-quantise x."""
     layout = LAYOUTS.get(layout, layout)
     r, c = (x.shape[0], x.shape[1]) if layout == ROW_1D else (x.shape[1], x.shape[0])
-    return mxfp4_quantize(x, layout, empty_mxtensor(r, c, x.device), stream)
+    with _on_stream(stream):
+        out = empty_mxtensor(r, c, x.device)
+    return mxfp4_quantize(x, layout, out, stream)
 
 
 def mx_gemm(a: MXTensor, b: MXTensor, out_dtype="f32", stream=None):
     import torch
     dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
-    c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
+    with _on_stream(stream):
+        c = torch.empty((a.rows, b.rows), dtype=dt, device=a.codes.device)
     return mxfp4_gemm(a, b, c, stream)

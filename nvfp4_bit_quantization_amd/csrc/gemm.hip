@@ -47,6 +47,28 @@ __device__ __forceinline__ half8v expand8(uint32_t q, _Float16 s) {
   return r;
 }
 
+// The epilogue's division by S_A S_B, without forming that product in
+// binary32: it overflows when both per-tensor maxima are small (about 1e-16
+// each) and underflows when both are large, although C itself is
+// representable.  S_A S_B = m 2^e with m = ma mb in [1/4, 1) (frexp), so
+// C = ldexp(acc * (1/m), -e): one rounded multiply (1/m lies in (1, 4]), then
+// an exact power-of-two scaling whenever C is a normal binary32.
+struct EpiScale {
+  float inv_m;
+  int neg_e;
+};
+
+__device__ __forceinline__ EpiScale epi_scale(const GemmArgs &g) {
+  int ea, eb;
+  const float ma = frexpf(*g.a_S, &ea), mb = frexpf(*g.b_S, &eb);
+  EpiScale s;
+  s.inv_m = 1.0f / (ma * mb);
+  s.neg_e = -(ea + eb);
+  return s;
+}
+
+__device__ __forceinline__ float epi_apply(float acc, const EpiScale &s) { return ldexpf(acc * s.inv_m, s.neg_e); }
+
 __device__ __forceinline__ _Float16 scale_f16(uint32_t scales4, int blk) {
   // E4M3 byte -> fp32 (exact) -> fp16 (exact: 2^-9 .. 448 are fp16 normals)
   const uint32_t b = (scales4 >> (8 * blk)) & 0xFFu;
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_generic_kernel(GemmArgs g) {
 
   // epilogue: C = acc / (S_A S_B); outputs past M or N are zero (zero
   // operands), so they do not change the fused maxima
-  const float inv = 1.0f / (*g.a_S * *g.b_S);
+  const EpiScale es = epi_scale(g);
   const bool fused = g.c_bf16 && (g.amax_plain || g.amax_rht);
   FusedMax fm;
   if (fused) fused_max_init(fm, g, lane);
@@ -309,7 +331,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_generic_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * (TM * 32) + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        const float v = acc[i][j][r] * inv;
+        const float v = epi_apply(acc[i][j][r], es);
         hb[r] = bf16_rne_bits(v);
         if (m < g.M && n < g.N) {
           if (g.c_bf16)
@@ -608,7 +630,7 @@ __device__ __forceinline__ void fast_store_c(const GemmArgs &g, int64_t m0, int6
   const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lr = lane & 31, h = lane >> 5;
-  const float inv = 1.0f / (*g.a_S * *g.b_S);
+  const EpiScale es = epi_scale(g);
   uint32_t ldc = (uint32_t)g.ldc;
   asm volatile("" : "+s"(ldc));  // per-element offsets are formed here, not hoisted and kept live
   if (g.c_bf16) {
@@ -626,7 +648,7 @@ __device__ __forceinline__ void fast_store_c(const GemmArgs &g, int64_t m0, int6
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
           const uint32_t n = wn * 128 + j * 32 + lr;
-          hb[r] = bf16_rne_bits(acc[i][j][r] * inv);
+          hb[r] = bf16_rne_bits(epi_apply(acc[i][j][r], es));
           ct[m * ldc + n] = (uint16_t)hb[r];
         }
         if (fused) fused_max_block(fm, g, hb);
@@ -643,7 +665,7 @@ __device__ __forceinline__ void fast_store_c(const GemmArgs &g, int64_t m0, int6
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
           const uint32_t n = wn * 128 + j * 32 + lr;
-          ct[m * ldc + n] = acc[i][j][r] * inv;
+          ct[m * ldc + n] = epi_apply(acc[i][j][r], es);
         }
   }
 }
@@ -672,7 +694,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
 // ===========================================================================
 // Stream-K (fast path shapes whose tile count leaves compute units idle in
 // the last round): one persistent workgroup per compute unit, all resident
-// (a cooperative launch).  The first dp_tiles tiles (whole rounds) are done
+// (the LDS admits one per CU).  The first dp_tiles tiles (whole rounds) are done
 // as whole tiles, round by round, so that the workgroups of one XCD start
 // their tiles together and share K-slices in L2.  The remaining tiles' units
 // (tile, K-tile) are numbered tile by tile in the grouped order and dealt out
@@ -685,8 +707,9 @@ __global__ __launch_bounds__(kGThreads) void gemm_fast_kernel(GemmArgs g) {
 // depend on timing) and lowers the flag, leaving every flag zero for the next
 // launch; then it writes C.  Partials and flags use device-coherent (sc1)
 // accesses; a partial's writes complete (vmcnt) before its flag is raised.
-// Each wait is bounded (about a second); on time-out `err` is set and that
-// tile's result is invalid, but the launch always ends.
+// Each wait is bounded (about a second); on time-out `err` is set, that
+// tile's result is invalid and the late partial is neither added nor its flag
+// lowered, but the launch always ends.
 // ===========================================================================
 struct StreamK {
   uint32_t *flags;  // [G]
@@ -772,22 +795,33 @@ __global__ __launch_bounds__(kGThreads) void gemm_streamk_kernel(GemmArgs g, Str
     } else {
       // head: add the partials of the following workgroups whose (non-empty)
       // ranges start inside the tile
+      __shared__ uint32_t timed_out;
       for (uint32_t v = w + 1; v < G && U * v / G < tend; ++v) {
         if (U * (v + 1) / G == U * v / G) continue;  // an empty range wrote no partial
         if (threadIdx.x == 0) {
+          uint32_t late = 0;
           for (uint32_t spins = 0;
                __hip_atomic_load(sk.flags + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;) {
             __builtin_amdgcn_s_sleep(8);
             if (++spins == (1u << 22)) {
               __hip_atomic_store(sk.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              late = 1;
               break;
             }
           }
+          timed_out = late;
         }
         __syncthreads();
-        add_partial(acc, sk.slots + (size_t)v * 65536);
-        __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_store(sk.flags + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // On a time-out the slot holds no finished partial and the flag is
+        // left alone (workgroup v raises it later): the tile is invalid, the
+        // error word says so, and the caller zero-fills the workspace again
+        // before its next use.
+        if (!timed_out) {
+          add_partial(acc, sk.slots + (size_t)v * 65536);
+          __syncthreads();
+          if (threadIdx.x == 0) __hip_atomic_store(sk.flags + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();  // timed_out is read by every thread before it is written again
       }
       fast_store_c(g, m0, n0, acc);
     }
@@ -815,12 +849,12 @@ hipError_t launch_gemm(const GemmArgs &g, void *workspace, size_t workspace_byte
   // units idle.  (With fewer rounds the split tiles' pipeline refills and
   // partial sums cost more than the idle units of one short last round, which
   // also runs at a higher clock: measured on 5120x5120x8192.)
-  // a stream being captured into a graph gets whole tiles (the stream-K
-  // kernel's cooperative launch is not something to record in a graph)
+  // A stream being captured into a graph gets whole tiles: a replay must not
+  // depend on every workgroup of the persistent grid being resident.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &capture) != hipSuccess) {
     (void)hipGetLastError();
-    capture = hipStreamCaptureStatusActive;  // unknown: take the path that needs no cooperative launch
+    capture = hipStreamCaptureStatusActive;  // unknown: take the whole-tile path
   }
   int dev = 0, cus = 0;
   if (workspace && capture == hipStreamCaptureStatusNone && !getenv("NVFP4_GEMM_DATA_PARALLEL") &&
@@ -836,12 +870,20 @@ hipError_t launch_gemm(const GemmArgs &g, void *workspace, size_t workspace_byte
       sk.tiles = (uint32_t)tiles;
       sk.KT = (uint32_t)(g.K / kFBK);
       sk.dp_tiles = (uint32_t)((tiles / cus) * cus);  // whole rounds first
-      GemmArgs ga = g;
-      void *params[] = {&ga, &sk};
-      const hipError_t e = hipLaunchCooperativeKernel((const void *)gemm_streamk_kernel, dim3((uint32_t)cus),
-                                                      dim3(kGThreads), params, 0, s);
-      if (e == hipSuccess) return e;
-      (void)hipGetLastError();  // refused: fall back to whole tiles
+      // One workgroup per compute unit, launched as an ordinary kernel: its
+      // 108 KiB of LDS admits one per CU, so on a GPU that runs nothing
+      // else all are resident together.  A workgroup only ever waits for
+      // workgroups with a larger index, and each wait is bounded, so the
+      // launch ends even if some were held back (then the error word is set).
+      // (A cooperative launch would guarantee residency but costs 15-22 us
+      // per call, measured on the Wgrad and linear-step shapes.)
+      int per_cu = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_streamk_kernel, kGThreads, 0) == hipSuccess &&
+          per_cu >= 1) {
+        hipLaunchKernelGGL(gemm_streamk_kernel, dim3((uint32_t)cus), dim3(kGThreads), 0, s, g, sk);
+        return hipGetLastError();
+      }
+      (void)hipGetLastError();  // occupancy unknown: whole tiles
     }
   }
   hipLaunchKernelGGL((gemm_fast_kernel<TM, TN>), dim3((uint32_t)tiles), dim3(kGThreads), 0, s, g);

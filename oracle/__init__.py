@@ -90,6 +90,7 @@ def _load():
         "oracle_e2m1_encode_sr_array": (None, [P, P, i64, P]),
         "oracle_e4m3_encode_array": (None, [P, i64, P]),
         "oracle_e2m1_encode_rtn_bits": (None, [u32, u32, P]),
+        "oracle_e4m3_encode_bits": (None, [u32, u32, P]),
         "oracle_philox_array": (None, [P, P, i64, P]),
         "oracle_f64_to_bf16_array": (None, [P, i64, P]),
         "oracle_sr_uniform_array": (None, [u64, P, P, i64, P]),
@@ -165,6 +166,14 @@ def e2m1_encode_rtn_bits(start: int, count: int) -> np.ndarray:
     """RTN codes for the fp32 bit patterns start .. start+count-1 (0xFF for NaN/Inf)."""
     out = np.empty(count, dtype=np.uint8)
     _load().oracle_e2m1_encode_rtn_bits(start, count, _ptr(out))
+    return out
+
+
+def e4m3_encode_bits(start: int, count: int) -> np.ndarray:
+    """E4M3 codes for the fp32 bit patterns start .. start+count-1 (0xFF for
+    negative, NaN or Inf patterns)."""
+    out = np.empty(count, dtype=np.uint8)
+    _load().oracle_e4m3_encode_bits(start, count, _ptr(out))
     return out
 
 

@@ -600,6 +600,16 @@ void oracle_e2m1_encode_rtn_bits(uint32_t start, uint32_t count, uint8_t *out) {
     out[i] = isfinite(f) ? oracle_e2m1_encode_rtn(f) : 0xFF;
   }
 }
+/* all fp32 bit patterns in [start, start + count): E4M3 codes (0xFF for
+ * negative, NaN or Inf patterns, which the encoder does not take) */
+void oracle_e4m3_encode_bits(uint32_t start, uint32_t count, uint8_t *out) {
+  for (uint32_t i = 0; i < count; i++) {
+    uint32_t u = start + i;
+    float f;
+    memcpy(&f, &u, 4);
+    out[i] = (isfinite(f) && !signbit(f)) ? oracle_e4m3_encode(f) : 0xFF;
+  }
+}
 void oracle_philox_array(const uint32_t *keys, const uint32_t *ctrs, int64_t n, uint32_t *out) {
   for (int64_t i = 0; i < n; i++) oracle_philox4x32_10(keys + 2 * i, ctrs + 4 * i, out + 4 * i);
 }

@@ -219,3 +219,96 @@ def test_gemm_fast_path_at_its_offset_limit(nv):
     err = rel_frobenius(got, ref)
     say("offset limit rel err", err)
     assert err <= 1e-3
+
+
+# ------------------------------------------------------- extreme tensor scales
+# The per-tensor scales S_A = 2688 / amax_A and S_B = 2688 / amax_B enter C only
+# through the division by S_A S_B (page paragraph 2: the FP32 per-tensor scale
+# over the E4M3 block scales).  That product overflows binary32 once
+# amax_A amax_B < 2688^2 / FLT_MAX (about 2e-32), e.g. two gradient-like tensors
+# with maxima near 1e-16, although C itself (about K amax_A amax_B) is an
+# ordinary binary32 number; and it underflows once amax_A amax_B exceeds about
+# 5e51, where every non-zero C overflows binary32 but the zero entries must stay
+# zero.
+EXTREME_SHAPES = [(256, 256, 512), (48, 80, 112)]  # fast path, direct kernel
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("stds", [(1e-17, 1e-17), (3e-20, 2e-15)], ids=["both-1e-17", "3e-20-and-2e-15"])
+def test_gemm_tiny_tensor_maxima(nv, shape, dt, stds):
+    M, N, K = shape
+    say("gemm tiny maxima", shape, dt, stds)
+    a_bits = syn.normal(M, K, seed=M + 5 * K, std=stds[0])
+    b_bits = syn.normal(N, K, seed=N + 7 * K, std=stds[1])
+    qa, qb = quant(nv, a_bits, "row"), quant(nv, b_bits, "row")
+    c = host(nv.gemm(qa, qb, dt).float())
+    torch.cuda.synchronize()
+    ga, gb = gpu_q_as_dict(qa), gpu_q_as_dict(qb)
+    assert_bit_exact(ga, oracle.quantize(a_bits, "row"), "A")
+    assert_bit_exact(gb, oracle.quantize(b_bits, "row"), "B")
+    # the case this test is about: S_A S_B is not a finite binary32
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.float32(ga["S"]) * np.float32(gb["S"]))
+    ref = oracle.round_output(oracle.gemm_f64(ga, gb), dt)
+    assert np.all(np.isfinite(ref)) and np.count_nonzero(ref) > 0.9 * ref.size
+    err = rel_frobenius(c, ref)
+    say("rel err", err)
+    assert err <= (1e-5 if dt == "f32" else 1e-3), err
+
+
+def test_gemm_tiny_maxima_wgrad_operands(nv):
+    """A Wgrad product of two gradient-sized tensors along tokens, both with
+    the RHT (signs from seed 77), the first with stochastic rounding: maxima
+    around 1e-17 and 1e-16."""
+    tokens, h1, h2 = 512, 256, 256
+    say("gemm tiny maxima, RHT operands")
+    dy = syn.laplace(tokens, h1, seed=61, scale=2e-18)
+    xx = syn.normal(tokens, h2, seed=62, std=3e-17)
+    qa = quant(nv, dy, "col", "sr", True, 99, 77)
+    qb = quant(nv, xx, "col", "rtn", True, 0, 77)
+    c = host(nv.gemm(qa, qb, "f32"))
+    torch.cuda.synchronize()
+    ga, gb = gpu_q_as_dict(qa), gpu_q_as_dict(qb)
+    assert_rht_tolerance(ga, oracle.quantize(dy, "col", "sr", True, 99, 77), "dY")
+    assert_rht_tolerance(gb, oracle.quantize(xx, "col", "rtn", True, 0, 77), "X")
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.float32(ga["S"]) * np.float32(gb["S"]))
+    ref = oracle.round_output(oracle.gemm_f64(ga, gb), "f32")
+    err = rel_frobenius(c, ref)
+    say("rel err", err)
+    assert err <= 1e-5, err
+
+
+def _block_sparse_positive(rows, K, seed, std, shift):
+    """|N(0, std)| values; row r keeps only its 16-wide k-block (r + shift) mod (K/16)."""
+    bits = syn.normal(rows, K, seed=seed, std=std) & np.uint16(0x7FFF)
+    blk = (np.arange(K)[None, :] // 16) == ((np.arange(rows)[:, None] + shift) % (K // 16))
+    return np.where(blk, bits, np.uint16(0)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(256, 256, 128), (48, 80, 112)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_huge_tensor_maxima(nv, shape, dt):
+    """Maxima near 1e26 on both operands: S_A S_B underflows binary32.  The
+    operands are block-sparse and non-negative, so C is exactly zero wherever
+    the rows' k-blocks differ and far beyond the binary32 range wherever they
+    match: the oracle's once-rounded C is 0 or +inf, and the GPU must give the
+    same (no NaN from 0 times an infinite factor)."""
+    M, N, K = shape
+    say("gemm huge maxima", shape, dt)
+    a_bits = _block_sparse_positive(M, K, seed=M + K, std=1e26, shift=0)
+    b_bits = _block_sparse_positive(N, K, seed=N + 3 * K, std=1e26, shift=1)
+    qa, qb = quant(nv, a_bits, "row"), quant(nv, b_bits, "row")
+    c = host(nv.gemm(qa, qb, dt).float())
+    torch.cuda.synchronize()
+    ga, gb = gpu_q_as_dict(qa), gpu_q_as_dict(qb)
+    assert_bit_exact(ga, oracle.quantize(a_bits, "row"), "A")
+    assert_bit_exact(gb, oracle.quantize(b_bits, "row"), "B")
+    with np.errstate(under="ignore"):
+        assert np.float32(ga["S"]) * np.float32(gb["S"]) == 0.0
+    with np.errstate(over="ignore"):
+        ref = oracle.round_output(oracle.gemm_f64(ga, gb), dt)
+    assert np.count_nonzero(ref == 0) > 0 and np.count_nonzero(np.isinf(ref)) > 0
+    assert not np.isnan(c).any()
+    assert np.array_equal(c, ref), (np.count_nonzero(c != ref), c.size)
