@@ -141,6 +141,28 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
 size_t nvfp4_workspace_bytes(void);
 
 /*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The partial maxima
+ * live in a static device buffer of the library, 12 KiB
+ * (nvfp4_workspace_bytes()) on each GPU it runs on, held until the process
+ * ends; its device address is looked up on the first call for a device (the
+ * stream's device, or the current one for a NULL stream).  The buffer's size
+ * does not depend on the input (the amax pass writes at most 1024 partial
+ * maxima per mode), so every input nvfp4_quantize accepts fits; the call
+ * allocates nothing.
+ *   x, rows, cols, ld_x, outs, n_outs, stream: as nvfp4_quantize.
+ * Every call on one GPU shares that GPU's buffer, which keeps the last call's
+ * partial maxima (each call writes the ones it reads before reading them):
+ * calls that may overlap on one GPU (different streams, or host threads)
+ * race and can produce wrong global scales -- order them on one stream.
+ * Returns as nvfp4_quantize, or NVFP4_E_HIP if the buffer's device address
+ * cannot be obtained.
+ */
+int nvfp4_quantize_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
+                           int n_outs, void *stream);
+
+/*
  * nvfp4_dequantize -- y[r][c] = (e(code) * s_b) / S for the stored
  * orientation of q, as fp32 with row stride ld_y elements.
  * Defines: page paragraph 2 (block scale times element, over the per-tensor

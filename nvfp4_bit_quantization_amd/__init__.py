@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.nvfp4_quantize.restype = i32
     L.nvfp4_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(nvfp4_quant_output), i32, P, ctypes.c_size_t, P]
+    L.nvfp4_quantize_noalloc.restype = i32
+    L.nvfp4_quantize_noalloc.argtypes = [P, i64, i64, i64, ctypes.POINTER(nvfp4_quant_output), i32, P]
     L.nvfp4_workspace_bytes.restype = ctypes.c_size_t
     L.nvfp4_workspace_bytes.argtypes = []
     L.nvfp4_dequantize.restype = i32
@@ -209,6 +211,22 @@ def nvfp4_quantize(x, specs: Sequence[QuantSpec], outs: Sequence[QTensor], works
                               ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
                               _stream(stream))
     _check(st, "nvfp4_quantize")
+    return list(outs)
+
+
+def nvfp4_quantize_noalloc(x, specs: Sequence[QuantSpec], outs: Sequence[QTensor], stream=None) -> List[QTensor]:
+    """nvfp4_quantize with the library's static scratch instead of a
+    workspace (allocates nothing; calls overlapping on one GPU race)."""
+    assert len(specs) == len(outs) and 1 <= len(specs) <= 2
+    import torch
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    arr = (nvfp4_quant_output * len(specs))()
+    for i, (s, o) in enumerate(zip(specs, outs)):
+        arr[i] = nvfp4_quant_output(s.layout, s.rounding, int(s.rht), AMAX_GIVEN if s.amax_given else 0, s.sr_seed,
+                                    s.rht_seed, o.c_struct())
+    st = lib().nvfp4_quantize_noalloc(ctypes.c_void_p(x.data_ptr()), x.shape[0], x.shape[1], x.stride(0), arr,
+                                      len(specs), _stream(stream))
+    _check(st, "nvfp4_quantize_noalloc")
     return list(outs)
 
 

@@ -5,12 +5,52 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "nvfp4.h"
 #include "nvfp4_kernels.hpp"
 
 using namespace nvfp4;
 
+// Partial maxima of nvfp4_quantize_noalloc: the library's own copy of the
+// quantise workspace, one per GPU (each device holds its own instance until
+// the process ends).  In host code this name is not a device address; the
+// kernels get the address hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) float scratch[3 * kMaxParts];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device dev (looked up once per device, with
+// that device current; the caller's current device is restored).
+int scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_E_UNSUPPORTED;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) {
+    *out = p;
+    return NVFP4_OK;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return NVFP4_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return NVFP4_E_HIP;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return NVFP4_E_HIP;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return NVFP4_OK;
+}
 
 // Philox4x32-10 on the host, for the RHT sign mask (same published algorithm
 // as the device copy: Salmon et al., SC'11).
@@ -161,8 +201,15 @@ const char *nvfp4_status_string(int status) {
   }
 }
 
-int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
-                   int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// nvfp4_quantize; with check_only, the argument checks that do not concern
+// the workspace, and nothing else (nvfp4_quantize_noalloc runs them before it
+// looks up its scratch)
+int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                  const nvfp4_quant_output *outs, int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
   if (!x || !outs) return NVFP4_E_NULL;
   if (n_outs != 1 && n_outs != 2) return NVFP4_E_UNSUPPORTED;
   if (rows <= 0 || cols <= 0 || (rows % 16) || (cols % 16)) return NVFP4_E_SHAPE;
@@ -171,9 +218,11 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
   if ((rows / 16) * cols >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
   if (ld_x < cols) return NVFP4_E_LD;
   if (!aligned16(x) || (ld_x % 8)) return NVFP4_E_ALIGN;
-  if (!workspace) return NVFP4_E_WORKSPACE;
-  if (workspace_bytes < nvfp4_workspace_bytes()) return NVFP4_E_WORKSPACE;
-  if (!aligned16(workspace)) return NVFP4_E_ALIGN;
+  if (!check_only) {
+    if (!workspace) return NVFP4_E_WORKSPACE;
+    if (workspace_bytes < kWsBytes) return NVFP4_E_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_E_ALIGN;
+  }
 
   OutPlan p[2];
   for (int i = 0; i < n_outs; ++i) {
@@ -191,6 +240,7 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
     const int g0 = p[order[0]].geom, g1 = p[order[1]].geom;
     if (!((g0 == G_ROW && g1 == G_COL) || (g0 == G_TILE && g1 == G_TILE_T))) return NVFP4_E_UNSUPPORTED;
   }
+  if (check_only) return NVFP4_OK;
   for (int i = 0; i < n_outs; ++i) {
     if (!p[i].rht) continue;
     const uint32_t m = nvfp4_rht_sign_mask(outs[i].rht_seed);
@@ -248,6 +298,39 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
   e = launch_quantize(qa, p0.geom, p0.rht, p0.sr, p1.geom, p1.rht, p1.sr, s, &supported);
   if (!supported) return NVFP4_E_UNSUPPORTED;
   return finish(e, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
+                   int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
+  return quantize_impl(false, x, rows, cols, ld_x, outs, n_outs, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_quantize_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
+                           int n_outs, void *stream) {
+  static_assert(sizeof(scratch) >= kWsBytes, "the static scratch holds a whole quantise workspace");
+  // the arguments first, with nvfp4_quantize's checks; the scratch address is
+  // looked up only for a call that will be launched
+  const int chk = quantize_impl(true, x, rows, cols, ld_x, outs, n_outs, nullptr, 0, stream);
+  if (chk != NVFP4_OK) return chk;
+  hipStream_t s = (hipStream_t)stream;
+  int dev = -1;
+  if (s) {
+    if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return NVFP4_E_HIP;
+    }
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return NVFP4_E_HIP;
+  }
+  void *ws = nullptr;
+  const int st = scratch_address(dev, &ws);
+  if (st != NVFP4_OK) return st;
+  return quantize_impl(false, x, rows, cols, ld_x, outs, n_outs, ws, sizeof(scratch), stream);
 }
 
 int nvfp4_dequantize(const nvfp4_tensor *q, float *y, int64_t ld_y, void *stream) {

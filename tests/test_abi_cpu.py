@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_workspace_bytes", "nvfp4_rht_sign_mask",
+    for n in ("nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_workspace_bytes",
+              "nvfp4_rht_sign_mask",
               "nvfp4_status_string", "nvfp4_codec_selftest", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm"):
         assert n in names
 
@@ -93,6 +94,29 @@ def test_quantize_argument_validation(L):
     # 16-element blocks are numbered in 31 bits: rows/16 * cols < 2^31
     big_r, big_c = 1 << 20, 1 << 15
     assert _q(L, [_out(nv.ROW_1D, big_r, big_c, nv.SCALE_1D16)], rows=big_r, cols=big_c, ld=big_c) == -2
+
+
+def _qn(L, outs, x=FAKE, rows=64, cols=32, ld=32):
+    arr = (nv.nvfp4_quant_output * max(1, len(outs)))(*outs)
+    return L.nvfp4_quantize_noalloc(ctypes.c_void_p(x), rows, cols, ld, arr, len(outs), None)
+
+
+def test_quantize_noalloc_argument_validation(L):
+    """The allocation-free entry point checks its arguments as nvfp4_quantize
+    does, before it looks up its scratch (no GPU is needed for these)."""
+    row = _out(nv.ROW_1D, 64, 32, nv.SCALE_1D16)
+    col = _out(nv.COL_1D, 32, 64, nv.SCALE_1D16)
+    assert _qn(L, [row], x=0) == -1
+    assert _qn(L, [row], rows=24) == -2
+    assert _qn(L, [row], ld=16) == -3
+    assert _qn(L, [row], x=FAKE + 8) == -4
+    assert _qn(L, [row, col, row]) == -5
+    assert _qn(L, [_out(nv.TWO_D, 64, 32, nv.SCALE_2D16, rht=1)]) == -5
+    assert _qn(L, [_out(nv.ROW_1D, 32, 64, nv.SCALE_1D16)]) == -2
+    assert _qn(L, [row, row]) == -5
+    arr = (nv.nvfp4_quant_output * 1)(row)
+    assert L.nvfp4_quantize_noalloc(None, 64, 32, 32, arr, 1, None) == -1
+    assert L.nvfp4_quantize_noalloc(ctypes.c_void_p(FAKE), 64, 32, 32, None, 1, None) == -1
 
 
 def test_dequantize_and_gemm_validation(L):
