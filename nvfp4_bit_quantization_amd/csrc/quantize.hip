@@ -90,7 +90,7 @@ __global__ void codec_selftest_kernel(int which, const float *in, const uint16_t
     if (which == 0)
       c = NVFP4_CVT_PK_FP4(0u, v, 0.0f, 0) & 0xFu;
     else if (which == 1)
-      c = e2m1_sr(v, u16[i]);
+      c = e2m1_sr_hw(v, u16[i], (int)(i & 1));
     else
       c = e4m3_encode(v);
     out[i] = (uint8_t)c;

@@ -191,21 +191,24 @@ __device__ __forceinline__ uint32_t pack8_rtn(const float v[8], float rb) {
   return w;
 }
 
-// 8 values -> word, SR with the uniforms of draw w[] (value k uses u16_of(w, k));
-// the sign bits come from the nearest-even conversion of the same values, which
-// keeps the sign of every value, zero included
+// 8 values -> word, SR with the uniforms of draw w[] (value k uses u16_of(w, k)),
+// on the hardware conversion (e2m1_sr_hw): word j of the draw holds the
+// uniforms of values 2j (low half) and 2j+1 (high half); the even values are
+// converted into the low nibbles of bytes 0..3, the odd ones into the high
+// nibbles, and the two words are merged.
+template <int J>
+__device__ __forceinline__ void sr_pair(const float v[8], float rb, const uint32_t w[4], uint32_t &lo, uint32_t &hi) {
+  const uint32_t nw = ~w[J];
+  lo = cvt_sr_fp4<J>(lo, sr_hw_prepare(v[2 * J] * rb), 0.0f, sr_hw_rand_lo(nw));
+  hi = cvt_sr_fp4<J>(hi, 0.0f, sr_hw_prepare(v[2 * J + 1] * rb), sr_hw_rand_hi(nw));
+}
 __device__ __forceinline__ uint32_t pack8_sr(const float v[8], float rb, const uint32_t w[4]) {
-  float y[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = v[k] * rb;
-  uint32_t mag = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) mag |= e2m1_sr_mag(y[k], u16_of(w, k)) << (4 * k);
-  uint32_t sgn = NVFP4_CVT_PK_FP4(0u, y[0], y[1], 0);
-  sgn = NVFP4_CVT_PK_FP4(sgn, y[2], y[3], 1);
-  sgn = NVFP4_CVT_PK_FP4(sgn, y[4], y[5], 2);
-  sgn = NVFP4_CVT_PK_FP4(sgn, y[6], y[7], 3);
-  return mag | (sgn & 0x88888888u);
+  uint32_t lo = 0u, hi = 0u;
+  sr_pair<0>(v, rb, w, lo, hi);
+  sr_pair<1>(v, rb, w, lo, hi);
+  sr_pair<2>(v, rb, w, lo, hi);
+  sr_pair<3>(v, rb, w, lo, hi);
+  return lo | hi;
 }
 
 __device__ __forceinline__ float block_scale(float bmax, float S, const float *lut, uint32_t *code) {
@@ -333,7 +336,7 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
           for (int i = 0; i < 16; ++i) {
             uint32_t w[4];
             sr_draw(o.sr_seed, (uint32_t)((L.r0 + i) * nbc + L.c0 / 16), L.hi, w);
-            const uint32_t code = e2m1_sr(v[i] * rb, u16_of(w, j));
+            const uint32_t code = e2m1_sr_hw(v[i] * rb, u16_of(w, j), 0);
             if (i < 8)
               lo |= code << (4 * i);
             else

@@ -64,6 +64,31 @@ def activation(rows: int = 8192, cols: int = HIDDEN, seed: int = 202, outlier_fr
     return f32_to_bf16_bits(x)
 
 
+def token_outlier_gradient(rows: int, cols: int, seed: int, scale: float = 1e-3, gain: float = 30.0,
+                           per_group: int = 1) -> np.ndarray:
+    """Laplace(0, scale) gradient [tokens][channels] in which, in every aligned
+    group of 16 tokens, `per_group` token rows (drawn without replacement
+    within the group) are multiplied by `gain`: outliers that sit in a few
+    tokens of each 16-token group, across all channels."""
+    g = _rng(seed)
+    x = g.laplace(0.0, scale, size=(rows, cols)).astype(np.float32)
+    for g0 in range(0, rows - rows % 16, 16):
+        x[g.choice(16, size=per_group, replace=False) + g0] *= np.float32(gain)
+    return f32_to_bf16_bits(x)
+
+
+def sparse_outlier_gradient(rows: int, cols: int, seed: int, scale: float = 1e-3, gain: float = 3e4,
+                            count: int = 64) -> np.ndarray:
+    """Laplace(0, scale) gradient with `count` entries, in distinct channels at
+    random tokens, multiplied by `gain`: rare outliers far above the bulk."""
+    g = _rng(seed)
+    x = g.laplace(0.0, scale, size=(rows, cols)).astype(np.float32)
+    ch = g.choice(cols, size=count, replace=False)
+    tk = g.integers(0, rows, size=count)
+    x[tk, ch] *= np.float32(gain)
+    return f32_to_bf16_bits(x)
+
+
 # The five workloads (shapes and distributions), keyed by name.
 WORKLOADS = {
     "tiny_256": dict(desc="bf16 256x256, N(0,1) + 4 outliers at +/-50; row 1D, RTN, then dequantize"),

@@ -91,6 +91,7 @@ def _load():
         "oracle_e4m3_encode_array": (None, [P, i64, P]),
         "oracle_e2m1_encode_rtn_bits": (None, [u32, u32, P]),
         "oracle_e4m3_encode_bits": (None, [u32, u32, P]),
+        "oracle_e2m1_sr_step_bits": (None, [u32, u32, P]),
         "oracle_philox_array": (None, [P, P, i64, P]),
         "oracle_f64_to_bf16_array": (None, [P, i64, P]),
         "oracle_sr_uniform_array": (None, [u64, P, P, i64, P]),
@@ -174,6 +175,15 @@ def e4m3_encode_bits(start: int, count: int) -> np.ndarray:
     negative, NaN or Inf patterns)."""
     out = np.empty(count, dtype=np.uint8)
     _load().oracle_e4m3_encode_bits(start, count, _ptr(out))
+    return out
+
+
+def e2m1_sr_step_bits(start: int, count: int) -> np.ndarray:
+    """For the fp32 bit patterns start .. start+count-1: the smallest u16 whose
+    stochastic-rounding code equals the code at u16 = 65535 (0 if all u16 give
+    one code); 0xFFFFFFFF for NaN/Inf patterns."""
+    out = np.empty(count, dtype=np.uint32)
+    _load().oracle_e2m1_sr_step_bits(start, count, _ptr(out))
     return out
 
 

@@ -610,6 +610,32 @@ void oracle_e4m3_encode_bits(uint32_t start, uint32_t count, uint8_t *out) {
     out[i] = (isfinite(f) && !signbit(f)) ? oracle_e4m3_encode(f) : 0xFF;
   }
 }
+/* all fp32 bit patterns in [start, start + count): the stochastic-rounding
+ * step of each value, i.e. the smallest u16 whose code equals the code at
+ * u16 = 65535 (0 when every u16 gives the same code), found by bisection on
+ * oracle_e2m1_encode_sr (the round-up set is a prefix of the u16 range);
+ * 0xFFFFFFFF for NaN or Inf patterns */
+void oracle_e2m1_sr_step_bits(uint32_t start, uint32_t count, uint32_t *out) {
+  for (uint32_t i = 0; i < count; i++) {
+    uint32_t u = start + i;
+    float f;
+    memcpy(&f, &u, 4);
+    if (!isfinite(f)) {
+      out[i] = 0xFFFFFFFFu;
+      continue;
+    }
+    const uint8_t last = oracle_e2m1_encode_sr(f, 0xFFFF);
+    uint32_t lo = 0, hi = 0xFFFF; /* the answer lies in [lo, hi] */
+    while (lo < hi) {
+      uint32_t mid = (lo + hi) / 2;
+      if (oracle_e2m1_encode_sr(f, (uint16_t)mid) == last)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    out[i] = lo;
+  }
+}
 void oracle_philox_array(const uint32_t *keys, const uint32_t *ctrs, int64_t n, uint32_t *out) {
   for (int64_t i = 0; i < n; i++) oracle_philox4x32_10(keys + 2 * i, ctrs + 4 * i, out + 4 * i);
 }

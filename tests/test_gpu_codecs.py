@@ -4,8 +4,10 @@ The E2M1 round-to-nearest path uses gfx950's FP32->FP4 conversion instruction,
 so it is checked exhaustively over all 2^32 binary32 bit patterns (NaN/Inf
 excluded).  The E4M3 block-scale encoder (software) is checked exhaustively
 over every non-negative finite binary32 pattern, the only inputs it takes.
-The stochastic-rounding encoder is checked on random (y, u16) pairs and on
-structured grids: every u16 against grid points, midpoints and neighbours.
+The stochastic-rounding encoder (the gfx950 SR conversion after an exact
+pre-rounding) is checked at every step point of every y with
+2^-17 <= |y| < 8, on random (y, u16) pairs and on structured grids (every
+u16 against grid points, midpoints and neighbours).
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -98,6 +100,66 @@ def test_e2m1_sr_encoder(nv):
     want = oracle.e2m1_encode_sr(ys, us)
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, (ys[bad[:5]], us[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def _sr_points(nv, pool, start, n, stride=1):
+    """Device against oracle stochastic rounding for the fp32 patterns
+    start, start + stride, ... (n of them), each at u16 = 0, step - 1, step
+    and 65535, step being where the oracle's rounding switches from up to
+    down.  Returns the number of (y, u16) pairs compared."""
+    sub = 1 << 22
+    if stride == 1:
+        bits = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32)
+        steps = np.concatenate(list(pool.map(lambda s0: oracle.e2m1_sr_step_bits(s0, min(sub, start + n - s0)),
+                                             range(start, start + n, sub))))
+    else:
+        bits = (start + stride * np.arange(n, dtype=np.uint64)).astype(np.uint32)
+        steps = np.array([oracle.e2m1_sr_step_bits(int(b), 1)[0] for b in bits], dtype=np.uint32)
+    y = bits.view(np.float32)
+    keep = steps != 0xFFFFFFFF
+    y, steps = y[keep], steps[keep]
+    u = np.stack([np.zeros_like(steps), np.maximum(steps, 1) - 1, np.minimum(steps, 65535),
+                  np.full_like(steps, 65535)], axis=1).astype(np.uint16)
+    ys = np.repeat(y, 4)
+    us = u.reshape(-1)
+    # the element index decides the instruction slot (even: first, odd: second);
+    # run every pair twice, shifted by one, so that both slots see every case
+    ys2, us2 = np.concatenate([ys, ys[:1], ys]), np.concatenate([us, us[:1], us])
+    x = torch.from_numpy(ys2).cuda()
+    uu = torch.from_numpy(us2.view(np.int16)).cuda()
+    out = torch.empty(ys2.size, dtype=torch.uint8, device="cuda")
+    nv.nvfp4_codec_selftest(1, x, uu, out)
+    got = host(out)
+    want = np.concatenate(list(pool.map(lambda i: oracle.e2m1_encode_sr(ys[i:i + sub], us[i:i + sub]),
+                                        range(0, ys.size, sub))))
+    for part, off in (("even slot", 0), ("odd slot", ys.size + 1)):
+        g = got[off:off + ys.size]
+        bad = np.flatnonzero(g != want)
+        assert bad.size == 0, "%s: y=%r u16=%d gpu %x oracle %x (%d mismatches)" % (
+            part, float(ys[bad[0]]), int(us[bad[0]]), g[bad[0]], want[bad[0]], bad.size)
+    return 2 * ys.size
+
+
+def test_e2m1_sr_hardware_path_at_every_step(nv):
+    """The stochastic-rounding encoder the kernels use (gfx950 conversion
+    instruction, after rounding |y| up to a multiple of 2^-23) against the
+    oracle's, for every binary32 y with 2^-17 <= |y| < 8, both signs: for each
+    y the oracle's round-up set is a prefix [0, step) of the u16 range, and
+    the device is checked at u16 = 0, step - 1, step and 65535, in both slots
+    of the instruction.  Below 2^-17 only u16 = 0 rounds up (a sampled check),
+    and 8 and above saturate like 6 (sampled)."""
+    pool = ThreadPoolExecutor(16)
+    lo, hi = 0x37000000, 0x41000000  # 2^-17 .. 8
+    chunk = 1 << 24
+    total = 0
+    for sign in (0, 0x80000000):
+        for start in range(lo, hi, chunk):
+            say("sr steps", hex(sign | start))
+            total += _sr_points(nv, pool, sign | start, min(chunk, hi - start))
+        total += _sr_points(nv, pool, sign | 0x00000001, 200000, stride=(lo - 1) // 200000)
+        total += _sr_points(nv, pool, sign | hi, 100000, stride=(0x7F7FFFFF - hi) // 100000)
+    say("sr steps: pairs compared", total)
+    assert total > 8 * (hi - lo)
 
 
 def test_sync_check_mode_in_a_child_process():
