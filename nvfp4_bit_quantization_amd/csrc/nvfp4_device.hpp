@@ -27,16 +27,11 @@ __device__ __forceinline__ float bf16_at(const uint4 &q, int k) {
 
 // ---------------------------------------------------------------- E4M3 ----
 // OCP E4M3FN, nearest-even, saturating at 448, subnormals m * 2^-9 kept.
-// s must be finite and >= 0.  Branch-free: both the normal and the subnormal
-// encodings are formed and the right one selected.
+// s must be finite and >= 0.  The gfx950 FP8 conversion (OCP E4M3FN,
+// nearest-even, subnormals kept) of min(s, 448): clamping first gives the
+// saturation (values from 448 up encode as 448, code 0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float s) {
-  const uint32_t u = __float_as_uint(s);
-  // normal range: round the 23-bit mantissa to 3 bits (ties to even), rebias 127 -> 7
-  const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  // below the smallest normal 2^-6: multiples of 2^-9 (exact scaling, then RNE)
-  const uint32_t sub = (uint32_t)__builtin_rintf(s * 512.0f);
-  const uint32_t c = s < 0.015625f ? sub : normal;
-  return s >= 448.0f ? 0x7Eu : c;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {

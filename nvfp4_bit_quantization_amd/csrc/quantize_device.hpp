@@ -211,8 +211,26 @@ __device__ __forceinline__ uint32_t pack8_sr(const float v[8], float rb, const u
   return lo | hi;
 }
 
+// bmax / 6 correctly rounded (binary32).  From 2^-120 up, the product with
+// the rounded reciprocal and one fused correction step give the correctly
+// rounded quotient for every input (checked over all non-negative binary32
+// values); below, where the quotient is near or in the subnormal range, the
+// division itself is used.
+__device__ __forceinline__ float div6(float x) {
+  const float r = 1.0f / 6.0f;
+  const float q0 = x * r;
+  float t = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, x), r, q0);
+  const bool slow = x < 0x1p-120f;
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) {  // a wave-uniform branch: rarely taken
+    float xs = x;
+    asm volatile("" : "+v"(xs));  // keeps the division inside the branch (not computed speculatively)
+    if (slow) t = xs / 6.0f;
+  }
+  return t;
+}
+
 __device__ __forceinline__ float block_scale(float bmax, float S, const float *lut, uint32_t *code) {
-  const float t = bmax / 6.0f;  // correctly rounded binary32 division
+  const float t = div6(bmax);
   const float sb = t * S;
   const uint32_t c = e4m3_encode(sb);
   *code = c;
