@@ -41,8 +41,7 @@ __device__ __forceinline__ float mx_inv_scale(uint32_t code) { return __uint_as_
 // ------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(kQThreads) void mx_quantize_kernel(MxQuantArgs a) {
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const Lane L = lane_coords(tile, a.R, a.C);
+  const Lane L = lane_coords(blockIdx.x, a.R, a.C);  // row-major tile order, as for NVFP4
   const uint32_t lane = threadIdx.x & 63;
   uint4 raw[16];
   if (L.valid) {

@@ -39,13 +39,25 @@ __global__ __launch_bounds__(kQThreads) __attribute__((
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const Lane L = lane_coords(tile, a.R, a.C);
+  const Lane L = lane_coords(blockIdx.x, a.R, a.C);  // tiles in row-major order: see quant_tiles
   uint4 raw[16];
   if (L.valid) load_micro_tile(a.x, a.ld, L, raw);
   quant_setup<NOUT>(a, (uint32_t)a.nparts, s_S, s_lut);
   if (!L.valid) return;
   quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut);
+}
+
+// 2D and 2D_T outputs, both rounded to nearest, from the same maximum (so
+// under the same global scale): the codes are computed once per element.
+__global__ __launch_bounds__(kQThreads) void quantize_tile_pair_kernel(QuantArgs a) {
+  __shared__ float s_lut[2][128];
+  __shared__ float s_S[2];
+  const Lane L = lane_coords(blockIdx.x, a.R, a.C);
+  uint4 raw[16];
+  if (L.valid) load_micro_tile(a.x, a.ld, L, raw);
+  quant_setup<2>(a, (uint32_t)a.nparts, s_S, s_lut);
+  if (!L.valid) return;
+  tile_pair_rtn(raw, L, a.o[0], a.o[1], s_S[0], s_lut[0], a.R, a.C);
 }
 
 // ------------------------------------------------------------------------
@@ -100,6 +112,11 @@ __global__ void codec_selftest_kernel(int which, const float *in, const uint16_t
 // ------------------------------------------------------------------------
 // host launchers
 // ------------------------------------------------------------------------
+// Quantise workgroups take their tiles in row-major order, one per block
+// index.  The tiles share no input, so dealing them to the XCDs in contiguous
+// ranges (as the GEMM does, for L2 reuse) gains nothing here; measured, it was
+// up to 5 % slower (2D + 2D_T outputs of a 5120 x 20480 weight), and other
+// orders (column-major, bands of 4-16 tile rows or columns) were no faster.
 int quant_tiles(int64_t R, int64_t C) {
   return (int)(((R + kQTileR - 1) / kQTileR) * ((C + kQTileC - 1) / kQTileC));
 }
@@ -155,6 +172,10 @@ hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int 
     if (rht0 && !rht1) return dispatch_row_col<true, false>(a, sr0, sr1, s);
     return dispatch_row_col<true, true>(a, sr0, sr1, s);
   } else if (g0 == G_TILE && g1 == G_TILE_T && !rht0 && !rht1) {
+    if (!sr0 && !sr1 && a.o[0].amax_in == a.o[1].amax_in && a.o[0].amax_mode == a.o[1].amax_mode) {
+      hipLaunchKernelGGL(quantize_tile_pair_kernel, dim3(quant_tiles(a.R, a.C)), dim3(kQThreads), 0, s, a);
+      return hipGetLastError();
+    }
     if (!sr0 && !sr1) return launch_q<G_TILE, false, false, G_TILE_T, false, false>(a, s);
     if (!sr0 && sr1) return launch_q<G_TILE, false, false, G_TILE_T, false, true>(a, s);
     if (sr0 && !sr1) return launch_q<G_TILE, false, true, G_TILE_T, false, false>(a, s);

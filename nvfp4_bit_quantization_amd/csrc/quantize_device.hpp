@@ -48,6 +48,15 @@ __device__ __forceinline__ void load_micro_tile(const uint16_t *x, int64_t ld, c
   for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4 *>(p + i * ld);
 }
 
+// An empty asm that claims to change the raw words: a later pass over the
+// micro-tile then unpacks bf16 -> fp32 again instead of keeping the 128
+// unpacked values of an earlier pass live, which would take 128 VGPRs and
+// cost waves per SIMD.
+__device__ __forceinline__ void opaque_raw(uint4 raw[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+}
+
 __device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -241,7 +250,7 @@ __device__ __forceinline__ float block_scale(float bmax, float S, const float *l
 // one output of the quantise pass
 // ------------------------------------------------------------------------
 template <int G, bool RHT, bool SR>
-__device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane &L, const OutArgs &o, float S,
+__device__ __forceinline__ void quantize_output(uint4 raw[16], const Lane &L, const OutArgs &o, float S,
                                                 const float *lut, int64_t R, int64_t C) {
   if (G == G_ROW) {
     const int64_t nbc = C / 16;
@@ -318,6 +327,7 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
 #pragma unroll
       for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(bf16_at(raw[i], k)));
     m = fmaxf(m, swap8(m));
+    opaque_raw(raw);
     uint32_t sc;
     const float rb = block_scale(m, S, lut, &sc);
     const int64_t nbc = C / 16, nbr = R / 16;
@@ -372,6 +382,67 @@ __device__ __forceinline__ void quantize_output(const uint4 raw[16], const Lane 
   }
 }
 
+// Transpose of an 8x8 matrix of nibbles held as 8 words (word i, nibble k) in
+// three steps: the off-diagonal 4x4 blocks (16-bit halves), then the 2x2
+// blocks inside each 4x4 (bytes), then single nibbles inside each 2x2.
+__device__ __forceinline__ void nibble_transpose8(uint32_t a[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = a[i], y = a[i + 4];
+    a[i] = (x & 0x0000FFFFu) | (y << 16);
+    a[i + 4] = (x >> 16) | (y & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i & 2) continue;
+    const uint32_t x = a[i], y = a[i + 2];
+    a[i] = (x & 0x00FF00FFu) | ((y & 0x00FF00FFu) << 8);
+    a[i + 2] = ((x >> 8) & 0x00FF00FFu) | (y & 0xFF00FF00u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t x = a[i], y = a[i + 1];
+    a[i] = (x & 0x0F0F0F0Fu) | ((y & 0x0F0F0F0Fu) << 4);
+    a[i + 1] = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+  }
+}
+
+// The 2D and 2D_T outputs under one global scale, both rounded to nearest:
+// every element gets the same code in both, so the codes are computed once,
+// row-packed for 2D, and the 2D_T words come from transposing the lane's two
+// 8x8 nibble matrices in registers.
+__device__ __forceinline__ void tile_pair_rtn(uint4 raw[16], const Lane &L, const OutArgs &o0,
+                                              const OutArgs &o1, float S, const float *lut, int64_t R, int64_t C) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(bf16_at(raw[i], k)));
+  m = fmaxf(m, swap8(m));
+  opaque_raw(raw);
+  uint32_t sc;
+  const float rb = block_scale(m, S, lut, &sc);
+  const int64_t nbc = C / 16, nbr = R / 16;
+  if (!L.hi) {
+    o0.scales[(L.r0 / 16) * nbc + L.c0 / 16] = (uint8_t)sc;
+    o1.scales[(L.c0 / 16) * nbr + L.r0 / 16] = (uint8_t)sc;
+  }
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = bf16_at(raw[i], k);
+    w[i] = pack8_rtn(v, rb);
+    *reinterpret_cast<uint32_t *>(o0.codes + (L.r0 + i) * (C / 2) + L.c0 / 2) = w[i];
+  }
+  nibble_transpose8(w);
+  nibble_transpose8(w + 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<uint2 *>(o1.codes + (L.c0 + j) * (R / 2) + L.r0 / 2) = make_uint2(w[j], w[8 + j]);
+}
+
 // Global scale of each output from the nparts partial maxima of its amax mode
 // (written by the amax pass) or from the maximum the caller gave, and the
 // table r(c) = S / E4M3(c) of element factors (0 for the zero scale).
@@ -420,6 +491,7 @@ __device__ __forceinline__ void quant_tile(uint4 raw[16], const Lane &L, const Q
                                            const float s_lut[2][128]) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
+  if (NOUT == 2 && !RHT0 && !RHT1) opaque_raw(raw);
   if (NOUT == 2 && !RHT1) quantize_output<G1, false, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
   if (RHT0) {
     if (G0 == G_COL)
