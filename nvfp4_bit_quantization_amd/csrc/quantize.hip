@@ -40,9 +40,11 @@ __global__ __launch_bounds__(kQThreads) __attribute__((
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
   const Lane L = lane_coords(blockIdx.x, a.R, a.C);  // tiles in row-major order: see quant_tiles
+  float pm[2][4];
+  load_partials<NOUT>(a, (uint32_t)a.nparts, pm);
   uint4 raw[16];
-  if (L.valid) load_micro_tile(a.x, a.ld, L, raw);
-  quant_setup<NOUT>(a, (uint32_t)a.nparts, s_S, s_lut);
+  load_micro_tile_any(a.x, a.ld, L, raw);
+  quant_setup<NOUT>(a, pm, s_S, s_lut);
   if (!L.valid) return;
   quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut);
 }
@@ -53,9 +55,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_tile_pair_kernel(QuantArgs
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
   const Lane L = lane_coords(blockIdx.x, a.R, a.C);
+  float pm[2][4];
+  load_partials<2>(a, (uint32_t)a.nparts, pm);
   uint4 raw[16];
-  if (L.valid) load_micro_tile(a.x, a.ld, L, raw);
-  quant_setup<2>(a, (uint32_t)a.nparts, s_S, s_lut);
+  load_micro_tile_any(a.x, a.ld, L, raw);
+  quant_setup<2>(a, pm, s_S, s_lut);
   if (!L.valid) return;
   tile_pair_rtn(raw, L, a.o[0], a.o[1], s_S[0], s_lut[0], a.R, a.C);
 }

@@ -47,6 +47,16 @@ __device__ __forceinline__ void load_micro_tile(const uint16_t *x, int64_t ld, c
 #pragma unroll
   for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4 *>(p + i * ld);
 }
+// The same without a branch: a lane past the tensor loads the micro-tile at
+// (0, 0), which always exists (both sizes are at least 16), and ignores it.
+// Without the branch the loads issued before the tile's (the partial maxima)
+// can be waited for alone.
+__device__ __forceinline__ void load_micro_tile_any(const uint16_t *x, int64_t ld, const Lane &L, uint4 raw[16]) {
+  Lane M = L;
+  M.r0 = L.valid ? L.r0 : 0;
+  M.c0 = L.valid ? L.c0 : 0;
+  load_micro_tile(x, ld, M, raw);
+}
 
 // An empty asm that claims to change the raw words: a later pass over the
 // micro-tile then unpacks bf16 -> fp32 again instead of keeping the 128
@@ -57,10 +67,22 @@ __device__ __forceinline__ void opaque_raw(uint4 raw[16]) {
   for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
 }
 
+// maximum over the wave, returned in every lane: DPP within each row of 16
+// lanes, then the four row maxima read as scalars (no LDS round trips)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  return m;
+  m = fmaxf(m, dpp_f<0xB1>(m));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, dpp_f<0x4E>(m));   // quad_perm [2,3,0,1]
+  m = fmaxf(m, dpp_f<0x124>(m));  // row_ror:4
+  m = fmaxf(m, dpp_f<0x128>(m));  // row_ror:8
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // ------------------------------------------------------------------------
@@ -443,43 +465,59 @@ __device__ __forceinline__ void tile_pair_rtn(uint4 raw[16], const Lane &L, cons
     *reinterpret_cast<uint2 *>(o1.codes + (L.c0 + j) * (R / 2) + L.r0 / 2) = make_uint2(w[j], w[8 + j]);
 }
 
-// Global scale of each output from the nparts partial maxima of its amax mode
-// (written by the amax pass) or from the maximum the caller gave, and the
-// table r(c) = S / E4M3(c) of element factors (0 for the zero scale).
+// This thread's share of the nparts partial maxima of each output's amax mode
+// (written by the amax pass), or the maximum the caller gave (thread 0).  The
+// loads are independent and are issued before the micro-tile's, so that
+// waiting for them does not wait for the tile.
+static_assert(kMaxParts <= 4 * kQThreads, "four partial maxima per thread at most");
 template <int NOUT>
-__device__ __forceinline__ void quant_setup(const QuantArgs &a, uint32_t nparts, float s_S[2],
-                                            float s_lut[2][128]) {
-  __shared__ float s_red[kQThreads / 64];
-  const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void load_partials(const QuantArgs &a, uint32_t nparts, float pm[2][4]) {
 #pragma unroll
   for (int o = 0; o < NOUT; ++o) {
     const float *part = a.partials + a.o[o].amax_mode * kMaxParts;
-    float m = 0.0f;
-    if (a.o[o].amax_in) {  // given by the caller (producer-fused)
-      if (threadIdx.x == 0) m = *a.o[o].amax_in;
-    } else {
-      for (uint32_t p = threadIdx.x; p < nparts; p += kQThreads) m = fmaxf(m, part[p]);
+    const bool given = a.o[o].amax_in != nullptr;  // producer-fused
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t p = threadIdx.x + k * kQThreads;
+      pm[o][k] = (!given && p < nparts) ? part[p] : 0.0f;
     }
-    m = wave_max(m);
-    if (lane == 0) s_red[w] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float amax = s_red[0];
-      for (int i = 1; i < kQThreads / 64; ++i) amax = fmaxf(amax, s_red[i]);
-      float S = 2688.0f / amax;  // 448 * 6
-      if (amax == 0.0f || !__builtin_isfinite(S)) S = 1.0f;
-      s_S[o] = S;
-      if (blockIdx.x == 0) {
-        *a.o[o].S_out = S;
-        *a.o[o].amax_out = amax;
-      }
+    if (given && threadIdx.x == 0) pm[o][0] = *a.o[o].amax_in;
+  }
+}
+
+// Global scale of each output from its partial maxima (load_partials), and
+// the table r(c) = S / E4M3(c) of element factors (0 for the zero scale).
+// Threads 0-127 build output 0's table, threads 128-255 output 1's; each
+// thread derives its output's S itself from the wave maxima, so two barriers
+// serve both outputs.
+static_assert(kQThreads == 256, "one half of the workgroup per output table");
+template <int NOUT>
+__device__ __forceinline__ void quant_setup(const QuantArgs &a, const float pm[2][4], float s_S[2],
+                                            float s_lut[2][128]) {
+  __shared__ float s_red[2][kQThreads / 64];
+  const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 0; o < NOUT; ++o) {
+    const float m = wave_max(fmaxf(fmaxf(pm[o][0], pm[o][1]), fmaxf(pm[o][2], pm[o][3])));
+    if (lane == 0) s_red[o][w] = m;
+  }
+  __syncthreads();
+  const uint32_t o = (NOUT == 2) ? (threadIdx.x >> 7) : 0u, c = threadIdx.x & 127u;
+  float amax = s_red[o][0];
+#pragma unroll
+  for (int i = 1; i < kQThreads / 64; ++i) amax = fmaxf(amax, s_red[o][i]);
+  float S = 2688.0f / amax;  // 448 * 6
+  if (amax == 0.0f || !__builtin_isfinite(S)) S = 1.0f;
+  if (threadIdx.x == 128u * o) {
+    s_S[o] = S;
+    if (blockIdx.x == 0) {
+      *a.o[o].S_out = S;
+      *a.o[o].amax_out = amax;
     }
-    __syncthreads();
-    if (threadIdx.x < 127) {
-      const float S = s_S[o];
-      const float val = e4m3_value(threadIdx.x);
-      s_lut[o][threadIdx.x] = (val == 0.0f) ? 0.0f : S / val;
-    }
+  }
+  if (c < 127u && (NOUT == 2 || threadIdx.x < 128u)) {
+    const float val = e4m3_value(c);
+    s_lut[o][c] = (val == 0.0f) ? 0.0f : S / val;
   }
   __syncthreads();
 }
