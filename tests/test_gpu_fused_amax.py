@@ -82,6 +82,27 @@ def test_gemm_amax_keeps_a_larger_value(nv):
     assert float(host(am)[0]) == np.float32(1.0e30)
 
 
+def test_2d_pair_with_given_amax(nv):
+    """The 2D + 2D_T pair computes each code once only when both outputs take
+    their maximum from the same source; with a given maximum on one or both
+    outputs the library runs the general kernel instead.  Both routes give the
+    oracle's outputs bit for bit."""
+    bits = syn.normal(272, 528, seed=78, std=0.02)
+    o2, o2t = oracle.quantize(bits, "2d"), oracle.quantize(bits, "2d_t")
+    x = dev_bf16(bits)
+    S = nv.QuantSpec.of
+    for given in ((False, False), (True, True), (True, False), (False, True)):
+        say("2d pair, given amax =", given)
+        specs = [S("2d", amax_given=given[0]), S("2d_t", amax_given=given[1])]
+        outs = [nv.empty_qtensor(272, 528, nv.SCALE_2D16), nv.empty_qtensor(528, 272, nv.SCALE_2D16)]
+        for q, g in zip(outs, given):
+            q.amax.fill_(float(o2["amax"]) if g else -1.0)  # ignored when not given
+        nv.nvfp4_quantize(x, specs, outs, nv.new_workspace())
+        torch.cuda.synchronize()
+        assert_bit_exact(gpu_q_as_dict(outs[0]), o2, "2d")
+        assert_bit_exact(gpu_q_as_dict(outs[1]), o2t, "2d_t")
+
+
 def test_quantize_with_given_amax(nv):
     """Given the oracle's maxima, the quantiser reproduces the oracle: the row
     output bit for bit, the RHT column output within the RHT tolerance, S
