@@ -2,8 +2,9 @@
 
 The E2M1 round-to-nearest path uses gfx950's FP32->FP4 conversion instruction,
 so it is checked exhaustively over all 2^32 binary32 bit patterns (NaN/Inf
-excluded).  The E4M3 block-scale encoder (software) is checked exhaustively
-over every non-negative finite binary32 pattern, the only inputs it takes.
+excluded).  The E4M3 block-scale encoder (gfx950's FP32->FP8 conversion after
+a clamp at 448) is checked exhaustively over every non-negative finite
+binary32 pattern, the only inputs it takes.
 The stochastic-rounding encoder (the gfx950 SR conversion after an exact
 pre-rounding) is checked at every step point of every y with
 2^-17 <= |y| < 8, on random (y, u16) pairs and on structured grids (every
