@@ -27,6 +27,16 @@ __device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t l
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
 }
 
+// a pointer the caller knows to be wave-uniform, in scalar registers (the
+// transfers take their base address from SGPRs).  The NVFP4 fast path moves
+// this base by the K-tile offset; the MXFP4 kernel, which issues its ten
+// transfers back to back, was 14 % slower that way and adds the offset per lane.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+  const uint64_t v = (uint64_t)p;
+  return (const uint8_t *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
+}
+
 // vmcnt <= n (other counters untouched)
 #define NVFP4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
