@@ -269,11 +269,60 @@ __device__ __forceinline__ float block_scale(float bmax, float S, const float *l
 }
 
 // ------------------------------------------------------------------------
+// row-layout output staged in LDS: the workgroup's 128 rows x 128 bytes of
+// codes and 128 x 16 scale bytes, written out afterwards as whole row segments
+// (a lane's own stores write 8 rows x 32 bytes per instruction)
+// ------------------------------------------------------------------------
+struct __align__(16) RowStage {
+  uint32_t codes[kQTileR * 32];  // dword d of row r at stage_dword(r, d)
+  uint8_t scales[kQTileR * 16];
+};
+// the 8 row groups of a wave write the same dword columns: an XOR of the
+// column by the row group spreads them over the LDS banks
+__device__ __forceinline__ uint32_t stage_dword(uint32_t r, uint32_t d) { return r * 32u + (d ^ (((r >> 4) & 3u) * 8u)); }
+
+// all threads of the workgroup, after a barrier; (tr0, tc0) is the tile origin
+__device__ __forceinline__ void row_stage_flush(const RowStage *st, const OutArgs &o, int64_t tr0, int64_t tc0,
+                                                int64_t R, int64_t C) {
+  const uint32_t t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // codes: thread t stores 16 bytes (32 elements) of row t/8 + 32k
+    const uint32_t row = (t >> 3) + 32u * k, chunk = t & 7u;
+    const int64_t r = tr0 + row, c = tc0 + chunk * 32;
+    if (r < R && c < C) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(st->codes + stage_dword(row, chunk * 4));
+      uint8_t *dst = o.codes + r * (C / 2) + c / 2;
+      if ((C & 31) == 0) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {  // rows start 8-byte aligned only; the last chunk may hold 16 elements
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(v.x, v.y);
+        if (c + 32 <= C) *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(v.z, v.w);
+      }
+    }
+  }
+  {  // scales: thread t stores the 8 block scales of half t&1 of row t/2
+    const uint32_t row = t >> 1, h = t & 1u;
+    const int64_t r = tr0 + row, nbc = C / 16, b0 = tc0 / 16 + h * 8;
+    if (r < R && b0 < nbc) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(st->scales + row * 16 + h * 8);
+      uint8_t *dst = o.scales + r * nbc + b0;
+      const int64_t n = nbc - b0 < 8 ? nbc - b0 : 8;
+      if (n == 8 && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+        *reinterpret_cast<uint2 *>(dst) = v;
+      } else {
+        const uint64_t w = ((uint64_t)v.y << 32) | v.x;
+        for (int64_t q = 0; q < n; ++q) dst[q] = (uint8_t)(w >> (8 * q));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
 // one output of the quantise pass
 // ------------------------------------------------------------------------
 template <int G, bool RHT, bool SR>
 __device__ __forceinline__ void quantize_output(uint4 raw[16], const Lane &L, const OutArgs &o, float S,
-                                                const float *lut, int64_t R, int64_t C) {
+                                                const float *lut, int64_t R, int64_t C, RowStage *st = nullptr) {
   if (G == G_ROW) {
     const int64_t nbc = C / 16;
 #pragma unroll
@@ -297,7 +346,15 @@ __device__ __forceinline__ void quantize_output(uint4 raw[16], const Lane &L, co
       if (RHT) rb *= 0.25f;
       const int64_t r = L.r0 + i;
       const uint32_t blk = (uint32_t)(r * nbc + L.c0 / 16);
-      if (!L.hi) o.scales[blk] = (uint8_t)sc;
+      // with a stage: the row within the tile and the dword column within its 128 bytes
+      const uint32_t lrow = (threadIdx.x & 7u) * 16u + i;
+      const uint32_t ldw = (threadIdx.x >> 6) * 8u + ((threadIdx.x & 63u) >> 3);
+      if (!L.hi) {
+        if (st)
+          st->scales[lrow * 16 + ldw / 2] = (uint8_t)sc;
+        else
+          o.scales[blk] = (uint8_t)sc;
+      }
       uint32_t word;
       if (SR) {
         uint32_t w[4];
@@ -306,7 +363,10 @@ __device__ __forceinline__ void quantize_output(uint4 raw[16], const Lane &L, co
       } else {
         word = pack8_rtn(v, rb);
       }
-      *reinterpret_cast<uint32_t *>(o.codes + r * (C / 2) + L.c0 / 2) = word;
+      if (st)
+        st->codes[stage_dword(lrow, ldw)] = word;
+      else
+        *reinterpret_cast<uint32_t *>(o.codes + r * (C / 2) + L.c0 / 2) = word;
     }
   } else if (G == G_COL) {
     const int64_t nbr = R / 16;
@@ -526,9 +586,9 @@ __device__ __forceinline__ void quant_setup(const QuantArgs &a, const float pm[2
 // ones with their sign vector XORed into the raw bf16 values (raw is changed).
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
 __device__ __forceinline__ void quant_tile(uint4 raw[16], const Lane &L, const QuantArgs &a, const float s_S[2],
-                                           const float s_lut[2][128]) {
+                                           const float s_lut[2][128], RowStage *st = nullptr) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
-  if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
+  if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C, st);
   if (NOUT == 2 && !RHT0 && !RHT1) opaque_raw(raw);
   if (NOUT == 2 && !RHT1) quantize_output<G1, false, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
   if (RHT0) {

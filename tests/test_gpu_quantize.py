@@ -301,6 +301,24 @@ def test_act_8192x5120_row_and_col(nv):
     check(nv, bits, [dict(layout="row"), dict(layout="col")], "act_8192x5120")
 
 
+def test_row_col_staged_ragged_strided(nv):
+    """The row + column RTN pair of tensors with at least 512 tiles stages its
+    row output in LDS and stores whole row segments.  A 4112 x 4112 input (561
+    tiles) has a partial last tile row and column, and 4112 columns are not a
+    multiple of 32, so the last 16-byte chunk of each row segment holds 16
+    elements; the input is read with a row stride of 4160.  Bit-exact."""
+    bits = syn.activation(4112, 4112, seed=91)
+    big = np.full((4112, 4160), 0x7F00, np.uint16)  # padding that would change every maximum if read
+    big[:, :4112] = bits
+    say("staged row+col 4112x4112, ld 4160")
+    x = dev_bf16(big)[:, :4112]
+    specs = [dict(layout="row"), dict(layout="col")]
+    outs = nv.quantize(x, [nv.QuantSpec.of(**d) for d in specs])
+    torch.cuda.synchronize()
+    for q, d in zip(outs, specs):
+        assert_bit_exact(gpu_q_as_dict(q), run_oracle(bits, d), "staged-" + d["layout"])
+
+
 def test_weight_5120x20480_2d(nv):
     """FFN weight 5120x20480, 2D 16x16 RTN plus the transposed copy; the
     transposed read dequantises bit-identically to the row read."""
