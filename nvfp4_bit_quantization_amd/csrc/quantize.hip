@@ -74,6 +74,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_row_col_staged_kernel(Quan
 
 // 2D and 2D_T outputs, both rounded to nearest, from the same maximum (so
 // under the same global scale): the codes are computed once per element.
+// With STAGE (large tensors) the 2D codes go through LDS as in the row + column
+// kernel above.
+template <bool STAGE>
 __global__ __launch_bounds__(kQThreads) void quantize_tile_pair_kernel(QuantArgs a) {
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
@@ -83,8 +86,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_tile_pair_kernel(QuantArgs
   uint4 raw[16];
   load_micro_tile_any(a.x, a.ld, L, raw);
   quant_setup<2>(a, pm, s_S, s_lut);
-  if (!L.valid) return;
-  tile_pair_rtn(raw, L, a.o[0], a.o[1], s_S[0], s_lut[0], a.R, a.C);
+  if constexpr (STAGE) {
+    __shared__ RowStage st;
+    if (L.valid) tile_pair_rtn(raw, L, a.o[0], a.o[1], s_S[0], s_lut[0], a.R, a.C, &st);
+    __syncthreads();  // every lane's 2D codes are in the stage
+    const int64_t ntc = (a.C + kQTileC - 1) / kQTileC;
+    row_stage_flush<false>(&st, a.o[0], (int64_t)(blockIdx.x / ntc) * kQTileR, (int64_t)(blockIdx.x % ntc) * kQTileC,
+                           a.R, a.C);
+  } else {
+    if (!L.valid) return;
+    tile_pair_rtn(raw, L, a.o[0], a.o[1], s_S[0], s_lut[0], a.R, a.C);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -204,7 +216,10 @@ hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int 
     return dispatch_row_col<true, true>(a, sr0, sr1, s);
   } else if (g0 == G_TILE && g1 == G_TILE_T && !rht0 && !rht1) {
     if (!sr0 && !sr1 && a.o[0].amax_in == a.o[1].amax_in && a.o[0].amax_mode == a.o[1].amax_mode) {
-      hipLaunchKernelGGL(quantize_tile_pair_kernel, dim3(quant_tiles(a.R, a.C)), dim3(kQThreads), 0, s, a);
+      if (quant_tiles(a.R, a.C) >= 512)
+        hipLaunchKernelGGL(quantize_tile_pair_kernel<true>, dim3(quant_tiles(a.R, a.C)), dim3(kQThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL(quantize_tile_pair_kernel<false>, dim3(quant_tiles(a.R, a.C)), dim3(kQThreads), 0, s, a);
       return hipGetLastError();
     }
     if (!sr0 && !sr1) return launch_q<G_TILE, false, false, G_TILE_T, false, false>(a, s);

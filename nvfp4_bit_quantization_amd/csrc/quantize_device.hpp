@@ -282,6 +282,7 @@ struct __align__(16) RowStage {
 __device__ __forceinline__ uint32_t stage_dword(uint32_t r, uint32_t d) { return r * 32u + (d ^ (((r >> 4) & 3u) * 8u)); }
 
 // all threads of the workgroup, after a barrier; (tr0, tc0) is the tile origin
+template <bool SCALES = true>
 __device__ __forceinline__ void row_stage_flush(const RowStage *st, const OutArgs &o, int64_t tr0, int64_t tc0,
                                                 int64_t R, int64_t C) {
   const uint32_t t = threadIdx.x;
@@ -300,7 +301,7 @@ __device__ __forceinline__ void row_stage_flush(const RowStage *st, const OutArg
       }
     }
   }
-  {  // scales: thread t stores the 8 block scales of half t&1 of row t/2
+  if (SCALES) {  // scales: thread t stores the 8 block scales of half t&1 of row t/2
     const uint32_t row = t >> 1, h = t & 1u;
     const int64_t r = tr0 + row, nbc = C / 16, b0 = tc0 / 16 + h * 8;
     if (r < R && b0 < nbc) {
@@ -494,7 +495,8 @@ __device__ __forceinline__ void nibble_transpose8(uint32_t a[8]) {
 // row-packed for 2D, and the 2D_T words come from transposing the lane's two
 // 8x8 nibble matrices in registers.
 __device__ __forceinline__ void tile_pair_rtn(uint4 raw[16], const Lane &L, const OutArgs &o0,
-                                              const OutArgs &o1, float S, const float *lut, int64_t R, int64_t C) {
+                                              const OutArgs &o1, float S, const float *lut, int64_t R, int64_t C,
+                                              RowStage *st = nullptr) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i)
@@ -516,7 +518,10 @@ __device__ __forceinline__ void tile_pair_rtn(uint4 raw[16], const Lane &L, cons
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = bf16_at(raw[i], k);
     w[i] = pack8_rtn(v, rb);
-    *reinterpret_cast<uint32_t *>(o0.codes + (L.r0 + i) * (C / 2) + L.c0 / 2) = w[i];
+    if (st)
+      st->codes[stage_dword((threadIdx.x & 7u) * 16u + i, (threadIdx.x >> 6) * 8u + ((threadIdx.x & 63u) >> 3))] = w[i];
+    else
+      *reinterpret_cast<uint32_t *>(o0.codes + (L.r0 + i) * (C / 2) + L.c0 / 2) = w[i];
   }
   nibble_transpose8(w);
   nibble_transpose8(w + 8);

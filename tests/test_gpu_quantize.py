@@ -301,18 +301,20 @@ def test_act_8192x5120_row_and_col(nv):
     check(nv, bits, [dict(layout="row"), dict(layout="col")], "act_8192x5120")
 
 
-def test_row_col_staged_ragged_strided(nv):
-    """The row + column RTN pair of tensors with at least 512 tiles stages its
-    row output in LDS and stores whole row segments.  A 4112 x 4112 input (561
-    tiles) has a partial last tile row and column, and 4112 columns are not a
-    multiple of 32, so the last 16-byte chunk of each row segment holds 16
-    elements; the input is read with a row stride of 4160.  Bit-exact."""
+@pytest.mark.parametrize("pair", [("row", "col"), ("2d", "2d_t")])
+def test_staged_pairs_ragged_strided(nv, pair):
+    """The RTN row + column and 2D + 2D_T pairs of tensors with at least 512
+    tiles stage their row-layout codes in LDS and store whole row segments.  A
+    4112 x 4112 input (561 tiles) has a partial last tile row and column, and
+    4112 columns are not a multiple of 32, so the last 16-byte chunk of each row
+    segment holds 16 elements; the input is read with a row stride of 4160.
+    Bit-exact."""
     bits = syn.activation(4112, 4112, seed=91)
     big = np.full((4112, 4160), 0x7F00, np.uint16)  # padding that would change every maximum if read
     big[:, :4112] = bits
-    say("staged row+col 4112x4112, ld 4160")
+    say("staged pair", pair, "4112x4112, ld 4160")
     x = dev_bf16(big)[:, :4112]
-    specs = [dict(layout="row"), dict(layout="col")]
+    specs = [dict(layout=pair[0]), dict(layout=pair[1])]
     outs = nv.quantize(x, [nv.QuantSpec.of(**d) for d in specs])
     torch.cuda.synchronize()
     for q, d in zip(outs, specs):
