@@ -29,13 +29,19 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(AmaxArgs a) {
 // extra waves hide more load latency than the larger register budget the
 // compiler would otherwise take buys (measured); the others keep their
 // allocation, which some of them need to avoid spills.
-template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
+template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1, bool STAGE>
 constexpr int quant_waves_per_simd() {
-  return ((G0 == G_COL && RHT0) || (G1 == G_COL && RHT1)) ? ((SR0 || SR1) ? 4 : 5) : 1;
+  return ((G0 == G_COL && RHT0) || (G1 == G_COL && RHT1)) ? ((SR0 || SR1 || STAGE) ? 4 : 5) : 1;
 }
-template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
-__global__ __launch_bounds__(kQThreads) __attribute__((
-    amdgpu_waves_per_eu(quant_waves_per_simd<G0, RHT0, SR0, G1, RHT1, SR1>()))) void quantize_kernel(QuantArgs a) {
+// With STAGE (row + column pairs of at least 512 tiles) the row output goes
+// through LDS and is stored as whole 128-byte row segments (row_stage_flush);
+// measured faster on every such pair (activation row + column 44.85 -> 43.17
+// us; 16384 x 5120 row + column with the RHT 87.7 -> 84.7 us), although the
+// stage's registers hold the RHT-column RTN pairs to four waves per SIMD.  On
+// small tensors the extra barrier costs more than it saves.
+template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1, bool STAGE = false>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(
+    quant_waves_per_simd<G0, RHT0, SR0, G1, RHT1, SR1, STAGE>()))) void quantize_kernel(QuantArgs a) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
@@ -45,37 +51,23 @@ __global__ __launch_bounds__(kQThreads) __attribute__((
   uint4 raw[16];
   load_micro_tile_any(a.x, a.ld, L, raw);
   quant_setup<NOUT>(a, pm, s_S, s_lut);
-  if (!L.valid) return;
-  quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut);
-}
-
-// Row + column outputs, both rounded to nearest and without the RHT, with the
-// row output staged in LDS and stored as whole 128-byte row segments.  On an
-// 8192 x 5120 activation the call took 43.4 us against 44.7 us unstaged; on
-// small tensors the extra barrier costs more than it saves, so the library
-// uses it from 512 tiles up.  (In the RHT instantiations the stage's
-// registers would take a wave per SIMD or spill.)
-__global__ __launch_bounds__(kQThreads) void quantize_row_col_staged_kernel(QuantArgs a) {
-  __shared__ float s_lut[2][128];
-  __shared__ float s_S[2];
-  __shared__ RowStage st;
-  const Lane L = lane_coords(blockIdx.x, a.R, a.C);
-  float pm[2][4];
-  load_partials<2>(a, (uint32_t)a.nparts, pm);
-  uint4 raw[16];
-  load_micro_tile_any(a.x, a.ld, L, raw);
-  quant_setup<2>(a, pm, s_S, s_lut);
-  if (L.valid) quant_tile<G_ROW, false, false, G_COL, false, false>(raw, L, a, s_S, s_lut, &st);
-  __syncthreads();  // every lane's row codes and scales are in the stage
-  const int64_t ntc = (a.C + kQTileC - 1) / kQTileC;
-  row_stage_flush(&st, a.o[0], (int64_t)(blockIdx.x / ntc) * kQTileR, (int64_t)(blockIdx.x % ntc) * kQTileC, a.R,
-                  a.C);
+  if constexpr (STAGE) {
+    __shared__ RowStage st;
+    if (L.valid) quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut, &st);
+    __syncthreads();  // every lane's row codes and scales are in the stage
+    const int64_t ntc = (a.C + kQTileC - 1) / kQTileC;
+    row_stage_flush(&st, a.o[0], (int64_t)(blockIdx.x / ntc) * kQTileR, (int64_t)(blockIdx.x % ntc) * kQTileC, a.R,
+                    a.C);
+  } else {
+    if (!L.valid) return;
+    quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut);
+  }
 }
 
 // 2D and 2D_T outputs, both rounded to nearest, from the same maximum (so
 // under the same global scale): the codes are computed once per element.
-// With STAGE (large tensors) the 2D codes go through LDS as in the row + column
-// kernel above.
+// With STAGE (from 512 tiles up) the 2D codes go through LDS as the row output
+// of the row + column kernels does (weight 2D + 2D_T 98.0 -> 92.9 us).
 template <bool STAGE>
 __global__ __launch_bounds__(kQThreads) void quantize_tile_pair_kernel(QuantArgs a) {
   __shared__ float s_lut[2][128];
@@ -178,6 +170,13 @@ hipError_t launch_amax(const AmaxArgs &a, bool plain, bool rc, bool rr, int npar
 
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
 static hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
+  if constexpr (G0 == G_ROW && G1 == G_COL) {
+    if (quant_tiles(a.R, a.C) >= 512) {
+      hipLaunchKernelGGL((quantize_kernel<G0, RHT0, SR0, G1, RHT1, SR1, true>), dim3(quant_tiles(a.R, a.C)),
+                         dim3(kQThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((quantize_kernel<G0, RHT0, SR0, G1, RHT1, SR1>), dim3(quant_tiles(a.R, a.C)), dim3(kQThreads),
                      0, s, a);
   return hipGetLastError();
@@ -191,10 +190,6 @@ static hipError_t dispatch_single(const QuantArgs &a, bool sr, hipStream_t s) {
 // {ROW, COL} pairs: g0 = ROW, g1 = COL
 template <bool RHT0, bool RHT1>
 static hipError_t dispatch_row_col(const QuantArgs &a, bool sr0, bool sr1, hipStream_t s) {
-  if (!RHT0 && !RHT1 && !sr0 && !sr1 && quant_tiles(a.R, a.C) >= 512) {
-    hipLaunchKernelGGL(quantize_row_col_staged_kernel, dim3(quant_tiles(a.R, a.C)), dim3(kQThreads), 0, s, a);
-    return hipGetLastError();
-  }
   if (!sr0 && !sr1) return launch_q<G_ROW, RHT0, false, G_COL, RHT1, false>(a, s);
   if (!sr0 && sr1) return launch_q<G_ROW, RHT0, false, G_COL, RHT1, true>(a, s);
   if (sr0 && !sr1) return launch_q<G_ROW, RHT0, true, G_COL, RHT1, false>(a, s);

@@ -301,24 +301,35 @@ def test_act_8192x5120_row_and_col(nv):
     check(nv, bits, [dict(layout="row"), dict(layout="col")], "act_8192x5120")
 
 
-@pytest.mark.parametrize("pair", [("row", "col"), ("2d", "2d_t")])
+STAGED_PAIRS = [
+    [dict(layout="row"), dict(layout="col")],
+    [dict(layout="2d"), dict(layout="2d_t")],
+    [dict(layout="row"), dict(layout="col", rht=True, rht_seed=4321)],
+    [dict(layout="row", rounding="sr", sr_seed=1236), dict(layout="col", rounding="sr", rht=True, sr_seed=1237,
+                                                          rht_seed=4321)],
+]
+
+
+@pytest.mark.parametrize("pair", STAGED_PAIRS, ids=["row+col", "2d+2d_t", "row+col-rht", "row-sr+col-rht-sr"])
 def test_staged_pairs_ragged_strided(nv, pair):
-    """The RTN row + column and 2D + 2D_T pairs of tensors with at least 512
-    tiles stage their row-layout codes in LDS and store whole row segments.  A
+    """The row + column and 2D + 2D_T pairs of tensors with at least 512 tiles
+    stage their row-layout codes in LDS and store whole row segments.  A
     4112 x 4112 input (561 tiles) has a partial last tile row and column, and
     4112 columns are not a multiple of 32, so the last 16-byte chunk of each row
     segment holds 16 elements; the input is read with a row stride of 4160.
-    Bit-exact."""
+    Bit-exact (the RHT output within the RHT tolerance)."""
     bits = syn.activation(4112, 4112, seed=91)
     big = np.full((4112, 4160), 0x7F00, np.uint16)  # padding that would change every maximum if read
     big[:, :4112] = bits
     say("staged pair", pair, "4112x4112, ld 4160")
     x = dev_bf16(big)[:, :4112]
-    specs = [dict(layout=pair[0]), dict(layout=pair[1])]
-    outs = nv.quantize(x, [nv.QuantSpec.of(**d) for d in specs])
+    outs = nv.quantize(x, [nv.QuantSpec.of(**d) for d in pair])
     torch.cuda.synchronize()
-    for q, d in zip(outs, specs):
-        assert_bit_exact(gpu_q_as_dict(q), run_oracle(bits, d), "staged-" + d["layout"])
+    for q, d in zip(outs, pair):
+        if d.get("rht"):
+            assert_rht_tolerance(gpu_q_as_dict(q), run_oracle(bits, d), "staged-" + d["layout"])
+        else:
+            assert_bit_exact(gpu_q_as_dict(q), run_oracle(bits, d), "staged-" + d["layout"])
 
 
 def test_weight_5120x20480_2d(nv):
