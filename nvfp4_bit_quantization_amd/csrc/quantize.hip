@@ -45,7 +45,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
-  const Lane L = lane_coords(blockIdx.x, a.R, a.C);  // tiles in row-major order: see quant_tiles
+  // tiles in row-major order (see quant_tiles); 256 x 128 ones for a single column output
+  constexpr bool TALL = G0 == G_COL && G1 == G_NONE;
+  const Lane L = TALL ? lane_coords_tall(blockIdx.x, a.R, a.C) : lane_coords(blockIdx.x, a.R, a.C);
   float pm[2][4];
   load_partials<NOUT>(a, (uint32_t)a.nparts, pm);
   uint4 raw[16];
@@ -177,8 +179,10 @@ static hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((quantize_kernel<G0, RHT0, SR0, G1, RHT1, SR1>), dim3(quant_tiles(a.R, a.C)), dim3(kQThreads),
-                     0, s, a);
+  const int tiles = (G0 == G_COL && G1 == G_NONE)
+                        ? (int)(((a.R + kQTallR - 1) / kQTallR) * ((a.C + kQTallC - 1) / kQTallC))
+                        : quant_tiles(a.R, a.C);
+  hipLaunchKernelGGL((quantize_kernel<G0, RHT0, SR0, G1, RHT1, SR1>), dim3(tiles), dim3(kQThreads), 0, s, a);
   return hipGetLastError();
 }
 
