@@ -343,6 +343,8 @@ __global__ __launch_bounds__(256) void mx_gemm_fast_kernel(MxGemmArgs g) {
   }
   NVFP4_WAIT_VMCNT(0);  // the clamped transfers of the last iterations
 
+  // Non-temporal C stores, as in the NVFP4 GEMM: C goes to HBM while this
+  // MFMA-bound kernel runs, so the next kernel does not pay for write-back.
   uint32_t ldc = (uint32_t)g.ldc;
   asm volatile("" : "+s"(ldc));
   if (g.c_bf16) {
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256) void mx_gemm_fast_kernel(MxGemmArgs g) {
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3), n = wn * 128 + j * 32 + lr;
           const uint32_t u = __float_as_uint(acc[i][j][r]);
-          ct[m * ldc + n] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+          __builtin_nontemporal_store((uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16), &ct[m * ldc + n]);
         }
   } else {
     float *ct = reinterpret_cast<float *>(g.c) + m0 * g.ldc + n0;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(256) void mx_gemm_fast_kernel(MxGemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t m = wm * 128 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3), n = wn * 128 + j * 32 + lr;
-          ct[m * ldc + n] = acc[i][j][r];
+          __builtin_nontemporal_store(acc[i][j][r], &ct[m * ldc + n]);
         }
   }
 }
