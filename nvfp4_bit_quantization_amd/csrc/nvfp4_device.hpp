@@ -64,19 +64,17 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // The rounding-up of |y| is done at scale 2^23 (t = y * 2^23 is exact; the
 // ceiling is of |t|, with y's sign put back), and the instruction's scale
 // operand 2^23 divides it back exactly.  The sign is handled by the instruction (sign-magnitude,
-// -0 gives code 8).  Each call converts one value; the other slot gets 0.
+// -0 gives code 8).  Each call converts one value, in the first slot (so R is
+// used unrotated); the second slot gets +0, whose code is 0 under any R.
 __device__ __forceinline__ float sr_hw_prepare(float y) {
   const float t = y * 8388608.0f;  // 2^23
   return __builtin_copysignf(__builtin_ceilf(__builtin_fabsf(t)), t);
 }
-// the random operand for a value in the pair's first slot (u16 in bits 0..15
-// of w) and in its second slot (u16 in bits 16..31 of w, operand rotated right
-// by one so that the instruction's left rotation restores it); nw = ~w
+// the random operand R = ~(u16 << 16) | 0xFFFF for a uniform held in bits
+// 0..15 of a word w (lo) or in bits 16..31 (hi, where ~u16 already sits in
+// bits 31..16 of ~w); nw = ~w
 __device__ __forceinline__ uint32_t sr_hw_rand_lo(uint32_t nw) { return __builtin_amdgcn_alignbit(nw, 0xFFFFFFFFu, 16); }
-__device__ __forceinline__ uint32_t sr_hw_rand_hi(uint32_t nw) {
-  const uint32_t r = nw | 0xFFFFu;
-  return __builtin_amdgcn_alignbit(r, r, 1);
-}
+__device__ __forceinline__ uint32_t sr_hw_rand_hi(uint32_t nw) { return nw | 0xFFFFu; }
 typedef float nvfp4_float2 __attribute__((ext_vector_type(2)));
 // The conversion writes byte `SEL` of its destination and keeps the other
 // three (probed on the device).  The compiler's builtin for it does not tie
@@ -98,12 +96,13 @@ __device__ __forceinline__ uint32_t cvt_sr_fp4(uint32_t dst, float a, float b, u
   return dst;
 }
 
-// one element: code of y under uniform u16, through the slot the kernels use
-// for an element of that parity (even: first slot, odd: second slot)
+// one element: code of y under uniform u16, with the random operand built as
+// the kernels build it for an element of that parity (even: u16 in the low
+// half of its Philox word, odd: in the high half)
 __device__ __forceinline__ uint32_t e2m1_sr_hw(float y, uint32_t u16, int odd) {
   const float c = sr_hw_prepare(y);
   if (!odd) return cvt_sr_fp4<0>(0u, c, 0.0f, sr_hw_rand_lo(~u16)) & 0xFu;
-  return (cvt_sr_fp4<0>(0u, 0.0f, c, sr_hw_rand_hi(~(u16 << 16))) >> 4) & 0xFu;
+  return cvt_sr_fp4<0>(0u, c, 0.0f, sr_hw_rand_hi(~(u16 << 16))) & 0xFu;
 }
 
 // -------------------------------------------------------------- Philox ----

@@ -242,14 +242,17 @@ __device__ __forceinline__ uint32_t pack8_rtn(const float v[8], float rb) {
 
 // 8 values -> word, SR with the uniforms of draw w[] (value k uses u16_of(w, k)),
 // on the hardware conversion (e2m1_sr_hw): word j of the draw holds the
-// uniforms of values 2j (low half) and 2j+1 (high half); the even values are
-// converted into the low nibbles of bytes 0..3, the odd ones into the high
-// nibbles, and the two words are merged.
+// uniforms of values 2j (low half) and 2j+1 (high half).  The even and the
+// odd values each go through the conversion's first slot, into the low
+// nibbles of bytes 0..3 of their own word; the odd word is moved up a nibble
+// when the two are merged.  (The first slot in both chains lets every call
+// take its value in one fixed register pair whose second half is zero, and
+// the odd values' random operand is one OR.)
 template <int J>
 __device__ __forceinline__ void sr_pair(const float v[8], float rb, const uint32_t w[4], uint32_t &lo, uint32_t &hi) {
   const uint32_t nw = ~w[J];
   lo = cvt_sr_fp4<J>(lo, sr_hw_prepare(v[2 * J] * rb), 0.0f, sr_hw_rand_lo(nw));
-  hi = cvt_sr_fp4<J>(hi, 0.0f, sr_hw_prepare(v[2 * J + 1] * rb), sr_hw_rand_hi(nw));
+  hi = cvt_sr_fp4<J>(hi, sr_hw_prepare(v[2 * J + 1] * rb), 0.0f, sr_hw_rand_hi(nw));
 }
 __device__ __forceinline__ uint32_t pack8_sr(const float v[8], float rb, const uint32_t w[4]) {
   uint32_t lo = 0u, hi = 0u;
@@ -257,7 +260,7 @@ __device__ __forceinline__ uint32_t pack8_sr(const float v[8], float rb, const u
   sr_pair<1>(v, rb, w, lo, hi);
   sr_pair<2>(v, rb, w, lo, hi);
   sr_pair<3>(v, rb, w, lo, hi);
-  return lo | hi;
+  return lo | (hi << 4);  // the high nibbles of both words are 0 (the +0 slot)
 }
 
 // bmax / 6 correctly rounded (binary32).  From 2^-120 up, the product with
