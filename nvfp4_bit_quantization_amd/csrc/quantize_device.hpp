@@ -104,18 +104,15 @@ __device__ __forceinline__ float wave_max(float m) {
 }
 
 // ------------------------------------------------------------------------
-// RHT: sign vectors as XORs of the bf16 sign bits, then the butterflies
+// RHT: the random signs flip sign bits, then the butterflies
 // ------------------------------------------------------------------------
-// along rows: row i of the 16-row group gets d_i
-__device__ __forceinline__ void flip_rows(uint4 raw[16], uint32_t mask) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t f = ((mask >> i) & 1u) ? 0x80008000u : 0u;
-    raw[i].x ^= f;
-    raw[i].y ^= f;
-    raw[i].z ^= f;
-    raw[i].w ^= f;
-  }
+// element k of a micro-tile row as fp32, its sign bit flipped when s is
+// 0x80000000 (s = 0 or 0x80000000): the flip costs nothing beyond the
+// unpacking (a shift-add for the low half, since adding 2^31 flips bit 31,
+// and a three-input logic op for the high half)
+__device__ __forceinline__ float bf16_at_signed(const uint4 &q, int k, uint32_t s) {
+  const uint32_t w = (k >> 1) == 0 ? q.x : (k >> 1) == 1 ? q.y : (k >> 1) == 2 ? q.z : q.w;
+  return __uint_as_float((k & 1) ? ((w & 0xFFFF0000u) ^ s) : ((w << 16) + s));
 }
 // along columns: column j = 8 hi + k of the 16-column block gets d_j
 __device__ __forceinline__ void flip_cols(uint4 raw[16], uint32_t mask, uint32_t hi) {
@@ -132,10 +129,11 @@ __device__ __forceinline__ void flip_cols(uint4 raw[16], uint32_t mask, uint32_t
   }
 }
 
-// column j (16 rows, signs applied): H v in binary32 (the 1/4 is applied later)
-__device__ __forceinline__ void fwht_column(const uint4 raw[16], int j, float d[16]) {
+// column j (16 rows; row i of the 16-row group gets d_i, bit i of mask):
+// H D v in binary32 (the 1/4 is applied later)
+__device__ __forceinline__ void fwht_column(const uint4 raw[16], int j, uint32_t mask, float d[16]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) d[i] = bf16_at(raw[i], j);
+  for (int i = 0; i < 16; ++i) d[i] = bf16_at_signed(raw[i], j, ((mask >> i) & 1u) << 31);
   fwht16(d);
 }
 
@@ -170,21 +168,26 @@ __device__ __forceinline__ void fwht_row(const uint4 &row, uint32_t hi, float d[
 template <bool PLAIN, bool RC, bool RR>
 __device__ __forceinline__ void tile_maxes(const uint4 raw[16], const Lane &L, uint32_t mask_rows,
                                            uint32_t mask_cols, float &m_plain, float &m_rc, float &m_rr) {
-  if (PLAIN) {
+  if (PLAIN && !RC) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
       for (int k = 0; k < 8; ++k) m_plain = fmaxf(m_plain, fabsf(bf16_at(raw[i], k)));
   }
   if (RC) {
-    uint4 r[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = raw[i];
-    flip_rows(r, mask_rows);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float d[16];
-      fwht_column(r, j, d);
+      if (PLAIN) {  // the plain maximum from the same unpacked values: a sign flip keeps |x|
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          d[i] = bf16_at_signed(raw[i], j, ((mask_rows >> i) & 1u) << 31);
+          m_plain = fmaxf(m_plain, fabsf(d[i]));
+        }
+        fwht16(d);
+      } else {
+        fwht_column(raw, j, mask_rows, d);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) m_rc = fmaxf(m_rc, fabsf(d[i]));
     }
@@ -342,9 +345,12 @@ __device__ __forceinline__ void row_stage_flush(const RowStage *st, const OutArg
 // ------------------------------------------------------------------------
 // one output of the quantise pass
 // ------------------------------------------------------------------------
+// (mask_rows: the RHT signs of a column-block output, applied while
+// unpacking; a row-block output's signs are already in raw)
 template <int G, bool RHT, bool SR>
 __device__ __forceinline__ void quantize_output(uint4 raw[16], const Lane &L, const OutArgs &o, float S,
-                                                const float *lut, int64_t R, int64_t C, RowStage *st = nullptr) {
+                                                const float *lut, int64_t R, int64_t C, uint32_t mask_rows,
+                                                RowStage *st = nullptr) {
   if (G == G_ROW) {
     const int64_t nbc = C / 16;
 #pragma unroll
@@ -396,7 +402,7 @@ __device__ __forceinline__ void quantize_output(uint4 raw[16], const Lane &L, co
     for (int j = 0; j < 8; ++j) {
       float v[16];  // with the RHT: unnormalised sums, 1/4 folded as for rows
       if (RHT) {
-        fwht_column(raw, j, v);
+        fwht_column(raw, j, mask_rows, v);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = bf16_at(raw[i], j);
@@ -609,33 +615,34 @@ __device__ __forceinline__ void quant_setup(const QuantArgs &a, const float pm[2
 }
 
 // All outputs of one micro-tile: outputs without the RHT first, then the RHT
-// ones with their sign vector XORed into the raw bf16 values (raw is changed).
+// ones.  A column-block output applies its signs while unpacking; a row-block
+// output has its signs XORed into the raw bf16 values (undone if another
+// output follows).  Between passes raw is either changed by such a flip or
+// fenced by opaque_raw, so that the compiler does not keep one pass's
+// unpacked values live for the next.  (A fence before the first pass would
+// make every load land before any work starts, so there is none.)
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1>
 __device__ __forceinline__ void quant_tile(uint4 raw[16], const Lane &L, const QuantArgs &a, const float s_S[2],
                                            const float s_lut[2][128], RowStage *st = nullptr) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
-  if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C, st);
+  if (!RHT0) quantize_output<G0, false, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C, 0u, st);
   if (NOUT == 2 && !RHT0 && !RHT1) opaque_raw(raw);
-  if (NOUT == 2 && !RHT1) quantize_output<G1, false, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
+  if (NOUT == 2 && !RHT1) quantize_output<G1, false, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C, 0u);
   if (RHT0) {
-    if (G0 == G_COL)
-      flip_rows(raw, a.mask_rows);
-    else
+    if (G0 == G_COL) {
+      if (NOUT == 2 && !RHT1) opaque_raw(raw);  // the non-RHT output went first
+    } else {
       flip_cols(raw, a.mask_cols, L.hi);
-    quantize_output<G0, true, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C);
-    if (NOUT == 2 && RHT1) {  // undo
-      if (G0 == G_COL)
-        flip_rows(raw, a.mask_rows);
-      else
-        flip_cols(raw, a.mask_cols, L.hi);
     }
+    quantize_output<G0, true, SR0>(raw, L, a.o[0], s_S[0], s_lut[0], a.R, a.C, a.mask_rows);
+    if (NOUT == 2 && RHT1 && G0 != G_COL) flip_cols(raw, a.mask_cols, L.hi);  // undo
   }
   if (NOUT == 2 && RHT1) {
     if (G1 == G_COL)
-      flip_rows(raw, a.mask_rows);
+      opaque_raw(raw);  // another pass went first
     else
       flip_cols(raw, a.mask_cols, L.hi);
-    quantize_output<G1, true, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C);
+    quantize_output<G1, true, SR1>(raw, L, a.o[1], s_S[1], s_lut[1], a.R, a.C, a.mask_rows);
   }
 }
 
