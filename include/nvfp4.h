@@ -140,6 +140,44 @@ int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, cons
  * maxima of up to 1024 workgroups per amax mode). */
 size_t nvfp4_workspace_bytes(void);
 
+/* One job of nvfp4_quantize_batch: the arguments of one nvfp4_quantize call
+ * without its workspace. */
+typedef struct {
+  const void *x;                   /* device bf16 [rows][cols], row stride ld_x */
+  int64_t rows;
+  int64_t cols;
+  int64_t ld_x;
+  const nvfp4_quant_output *outs;  /* host array of n_outs (1 or 2) descriptors */
+  int32_t n_outs;
+} nvfp4_quant_job;
+
+/*
+ * nvfp4_quantize_batch -- several independent quantisations, each with
+ * exactly the outputs nvfp4_quantize gives for the same job (bit for bit),
+ * enqueued together on `stream`.
+ *
+ * Defines: page paragraph 2 (the quantisation of each job as for
+ * nvfp4_quantize; the weight-gradient GEMM's two inputs are quantised with
+ * the 16x16 RHT along the token dimension).
+ *   jobs       host array of n_jobs >= 1 job descriptors, each checked as
+ *              nvfp4_quantize checks its arguments.  Jobs must not write the
+ *              same output buffers.
+ *   workspace  device scratch of at least n_jobs * nvfp4_workspace_bytes()
+ *              bytes, 16-byte aligned (job j uses the j-th slice).
+ * Two jobs that each have a single NVFP4_COL_1D output with the RHT and
+ * flags 0 (the weight-gradient operand pair; either rounding for each) run as
+ * one amax launch and one quantise launch whose workgroups alternate between
+ * the two inputs, so that the arithmetic of one overlaps the memory traffic
+ * of the other.  Any other batch enqueues its jobs one after another, as
+ * nvfp4_quantize would.
+ * Returns NVFP4_OK or a negative status: NVFP4_E_NULL for jobs == NULL,
+ * NVFP4_E_UNSUPPORTED for n_jobs < 1, NVFP4_E_WORKSPACE or NVFP4_E_ALIGN for
+ * the workspace, else the first failing job's status.  Every job is checked
+ * before anything is enqueued.
+ */
+int nvfp4_quantize_batch(const nvfp4_quant_job *jobs, int n_jobs, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
 /*
  * nvfp4_quantize_noalloc -- nvfp4_quantize without a workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,

@@ -56,6 +56,11 @@ class nvfp4_quant_output(ctypes.Structure):
                 ("out", nvfp4_tensor)]
 
 
+class nvfp4_quant_job(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64),
+                ("outs", ctypes.POINTER(nvfp4_quant_output)), ("n_outs", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -71,6 +76,8 @@ def lib() -> ctypes.CDLL:
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.nvfp4_quantize.restype = i32
     L.nvfp4_quantize.argtypes = [P, i64, i64, i64, ctypes.POINTER(nvfp4_quant_output), i32, P, ctypes.c_size_t, P]
+    L.nvfp4_quantize_batch.restype = i32
+    L.nvfp4_quantize_batch.argtypes = [ctypes.POINTER(nvfp4_quant_job), i32, P, ctypes.c_size_t, P]
     L.nvfp4_quantize_noalloc.restype = i32
     L.nvfp4_quantize_noalloc.argtypes = [P, i64, i64, i64, ctypes.POINTER(nvfp4_quant_output), i32, P]
     L.nvfp4_workspace_bytes.restype = ctypes.c_size_t
@@ -188,10 +195,10 @@ def output_shape(rows: int, cols: int, layout: int):
     raise ValueError(layout)
 
 
-def new_workspace(device="cuda"):
-    """A quantise workspace (one per stream)."""
+def new_workspace(device="cuda", jobs=1):
+    """A quantise workspace (one per stream), for `jobs` jobs of a batch."""
     import torch
-    return torch.empty(lib().nvfp4_workspace_bytes() // 4, dtype=torch.float32, device=device)
+    return torch.empty(jobs * lib().nvfp4_workspace_bytes() // 4, dtype=torch.float32, device=device)
 
 
 # ---------------------------------------------------------------------------
@@ -212,6 +219,29 @@ def nvfp4_quantize(x, specs: Sequence[QuantSpec], outs: Sequence[QTensor], works
                               _stream(stream))
     _check(st, "nvfp4_quantize")
     return list(outs)
+
+
+def nvfp4_quantize_batch(jobs, workspace, stream=None):
+    """Several independent nvfp4_quantize calls enqueued together (see
+    include/nvfp4.h).  jobs: a sequence of (x, specs, outs); workspace: at
+    least len(jobs) * nvfp4_workspace_bytes() bytes (new_workspace(len(jobs)))."""
+    import torch
+    arrs = []
+    jarr = (nvfp4_quant_job * len(jobs))()
+    for j, (x, specs, outs) in enumerate(jobs):
+        assert len(specs) == len(outs) and 1 <= len(specs) <= 2
+        assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+        arr = (nvfp4_quant_output * len(specs))()
+        for i, (s, o) in enumerate(zip(specs, outs)):
+            arr[i] = nvfp4_quant_output(s.layout, s.rounding, int(s.rht), AMAX_GIVEN if s.amax_given else 0,
+                                        s.sr_seed, s.rht_seed, o.c_struct())
+        arrs.append(arr)  # kept alive until the call returns
+        jarr[j] = nvfp4_quant_job(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0),
+                                  ctypes.cast(arr, ctypes.POINTER(nvfp4_quant_output)), len(specs))
+    st = lib().nvfp4_quantize_batch(jarr, len(jobs), ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "nvfp4_quantize_batch")
+    return [list(outs) for _, _, outs in jobs]
 
 
 def nvfp4_quantize_noalloc(x, specs: Sequence[QuantSpec], outs: Sequence[QTensor], stream=None) -> List[QTensor]:

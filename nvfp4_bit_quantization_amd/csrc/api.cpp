@@ -205,11 +205,20 @@ const char *nvfp4_status_string(int status) {
 
 namespace {
 
-// nvfp4_quantize; with check_only, the argument checks that do not concern
-// the workspace, and nothing else (nvfp4_quantize_noalloc runs them before it
-// looks up its scratch)
-int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, int64_t ld_x,
-                  const nvfp4_quant_output *outs, int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
+// One quantise call, planned: its kernel arguments and what it launches.
+struct QuantCall {
+  QuantArgs qa;
+  AmaxArgs aa;
+  OutPlan p0, p1;        // the outputs in kernel order (ROW before COL, TILE before TILE_T)
+  bool plain, rc, rr;    // maxima the amax pass must produce
+};
+
+// nvfp4_quantize's argument checks, in this order: pointers and counts,
+// shape, leading dimension, alignment, the workspace (only with check_ws),
+// the outputs.  With `call`, also its kernel arguments (partial maxima in the
+// workspace).
+int plan_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
+                  int n_outs, bool check_ws, void *workspace, size_t workspace_bytes, QuantCall *call) {
   if (!x || !outs) return NVFP4_E_NULL;
   if (n_outs != 1 && n_outs != 2) return NVFP4_E_UNSUPPORTED;
   if (rows <= 0 || cols <= 0 || (rows % 16) || (cols % 16)) return NVFP4_E_SHAPE;
@@ -218,7 +227,7 @@ int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, in
   if ((rows / 16) * cols >= ((int64_t)1 << 31)) return NVFP4_E_SHAPE;
   if (ld_x < cols) return NVFP4_E_LD;
   if (!aligned16(x) || (ld_x % 8)) return NVFP4_E_ALIGN;
-  if (!check_only) {
+  if (check_ws) {
     if (!workspace) return NVFP4_E_WORKSPACE;
     if (workspace_bytes < kWsBytes) return NVFP4_E_WORKSPACE;
     if (!aligned16(workspace)) return NVFP4_E_ALIGN;
@@ -230,7 +239,6 @@ int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, in
     if (st != NVFP4_OK) return st;
   }
   int order[2] = {0, 1};
-  uint32_t mask_rows = 0, mask_cols = 0;
   if (n_outs == 2) {
     // canonical pair order: ROW before COL, TILE before TILE_T
     if ((p[0].geom == G_COL && p[1].geom == G_ROW) || (p[0].geom == G_TILE_T && p[1].geom == G_TILE)) {
@@ -240,7 +248,9 @@ int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, in
     const int g0 = p[order[0]].geom, g1 = p[order[1]].geom;
     if (!((g0 == G_ROW && g1 == G_COL) || (g0 == G_TILE && g1 == G_TILE_T))) return NVFP4_E_UNSUPPORTED;
   }
-  if (check_only) return NVFP4_OK;
+  if (!call) return NVFP4_OK;
+
+  uint32_t mask_rows = 0, mask_cols = 0;
   for (int i = 0; i < n_outs; ++i) {
     if (!p[i].rht) continue;
     const uint32_t m = nvfp4_rht_sign_mask(outs[i].rht_seed);
@@ -249,32 +259,27 @@ int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, in
     else
       mask_cols = m;
   }
-
-  hipStream_t s = (hipStream_t)stream;
   const int tiles = quant_tiles(rows, cols);
   float *partials = (float *)workspace;
-
-  QuantArgs qa;
+  QuantArgs &qa = call->qa;
   qa.x = (const uint16_t *)x;
   qa.R = rows;
   qa.C = cols;
   qa.ld = ld_x;
   qa.partials = partials;
+  qa.nparts = tiles < kMaxParts ? tiles : kMaxParts;
   qa.mask_rows = mask_rows;
   qa.mask_cols = mask_cols;
-  const OutPlan &p0 = p[order[0]];
-  qa.o[0] = out_args(outs[order[0]], p0.amax_mode);
-  OutPlan p1 = {G_NONE, false, false, AM_PLAIN};
+  call->p0 = p[order[0]];
+  qa.o[0] = out_args(outs[order[0]], call->p0.amax_mode);
+  call->p1 = OutPlan{G_NONE, false, false, AM_PLAIN};
   if (n_outs == 2) {
-    p1 = p[order[1]];
-    qa.o[1] = out_args(outs[order[1]], p1.amax_mode);
+    call->p1 = p[order[1]];
+    qa.o[1] = out_args(outs[order[1]], call->p1.amax_mode);
   } else {
     qa.o[1] = qa.o[0];
   }
-  bool supported = true;
-
-  const int nparts = tiles < kMaxParts ? tiles : kMaxParts;
-  AmaxArgs aa;
+  AmaxArgs &aa = call->aa;
   aa.x = (const uint16_t *)x;
   aa.R = rows;
   aa.C = cols;
@@ -282,22 +287,47 @@ int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, in
   aa.partials = partials;
   aa.mask_rows = mask_rows;
   aa.mask_cols = mask_cols;
-  bool plain = false, rc = false, rr = false;  // maxima the amax pass must produce
+  call->plain = call->rc = call->rr = false;
   for (int i = 0; i < n_outs; ++i) {
     if (outs[i].flags & NVFP4_AMAX_GIVEN) continue;
-    plain |= p[i].amax_mode == AM_PLAIN;
-    rc |= p[i].amax_mode == AM_RHT_COL;
-    rr |= p[i].amax_mode == AM_RHT_ROW;
+    call->plain |= p[i].amax_mode == AM_PLAIN;
+    call->rc |= p[i].amax_mode == AM_RHT_COL;
+    call->rr |= p[i].amax_mode == AM_RHT_ROW;
   }
-  hipError_t e = hipSuccess;
-  if (plain || rc || rr) {
-    e = launch_amax(aa, plain, rc, rr, nparts, s);
-    if (e != hipSuccess) return NVFP4_E_HIP;
+  return NVFP4_OK;
+}
+
+// enqueue a planned call: the amax pass (when a maximum is needed), then the
+// quantise pass
+int launch_call(const QuantCall &c, hipStream_t s) {
+  if (c.plain || c.rc || c.rr) {
+    if (launch_amax(c.aa, c.plain, c.rc, c.rr, c.qa.nparts, s) != hipSuccess) return NVFP4_E_HIP;
   }
-  qa.nparts = nparts;
-  e = launch_quantize(qa, p0.geom, p0.rht, p0.sr, p1.geom, p1.rht, p1.sr, s, &supported);
+  bool supported = true;
+  const hipError_t e = launch_quantize(c.qa, c.p0.geom, c.p0.rht, c.p0.sr, c.p1.geom, c.p1.rht, c.p1.sr, s, &supported);
   if (!supported) return NVFP4_E_UNSUPPORTED;
-  return finish(e, s);
+  return e == hipSuccess ? NVFP4_OK : NVFP4_E_HIP;
+}
+
+// nvfp4_quantize; with check_only, the argument checks that do not concern
+// the workspace, and nothing else (nvfp4_quantize_noalloc runs them before it
+// looks up its scratch)
+int quantize_impl(bool check_only, const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                  const nvfp4_quant_output *outs, int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
+  QuantCall c;
+  const int st = plan_quantize(x, rows, cols, ld_x, outs, n_outs, !check_only, workspace, workspace_bytes,
+                               check_only ? nullptr : &c);
+  if (st != NVFP4_OK || check_only) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int lst = launch_call(c, s);
+  if (lst != NVFP4_OK) return lst;
+  return finish(hipSuccess, s);
+}
+
+// a job of the Wgrad operand kind: one RHT column output, its maximum from
+// the amax pass
+bool wgrad_operand(const nvfp4_quant_job &j) {
+  return j.n_outs == 1 && j.outs[0].layout == NVFP4_COL_1D && j.outs[0].rht == 1 && j.outs[0].flags == 0;
 }
 
 }  // namespace
@@ -307,6 +337,38 @@ extern "C" {
 int nvfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,
                    int n_outs, void *workspace, size_t workspace_bytes, void *stream) {
   return quantize_impl(false, x, rows, cols, ld_x, outs, n_outs, workspace, workspace_bytes, stream);
+}
+
+int nvfp4_quantize_batch(const nvfp4_quant_job *jobs, int n_jobs, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  if (!jobs) return NVFP4_E_NULL;
+  if (n_jobs < 1) return NVFP4_E_UNSUPPORTED;
+  if (!workspace || workspace_bytes / kWsBytes < (size_t)n_jobs) return NVFP4_E_WORKSPACE;
+  if (!aligned16(workspace)) return NVFP4_E_ALIGN;
+  for (int j = 0; j < n_jobs; ++j) {  // every job is checked before anything is enqueued
+    const nvfp4_quant_job &b = jobs[j];
+    const int st = plan_quantize(b.x, b.rows, b.cols, b.ld_x, b.outs, b.n_outs, false, nullptr, 0, nullptr);
+    if (st != NVFP4_OK) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;  // job j's partial maxima in the j-th slice of kWsBytes
+  QuantCall c[2];
+  if (n_jobs == 2 && wgrad_operand(jobs[0]) && wgrad_operand(jobs[1])) {
+    for (int j = 0; j < 2; ++j) {
+      const nvfp4_quant_job &b = jobs[j];
+      const int st = plan_quantize(b.x, b.rows, b.cols, b.ld_x, b.outs, b.n_outs, true, ws + j * kWsBytes, kWsBytes,
+                                   &c[j]);
+      if (st != NVFP4_OK) return st;
+    }
+    return finish(launch_quantize_batch2(c[0].aa, c[0].qa, c[0].p0.sr, c[1].aa, c[1].qa, c[1].p0.sr, s), s);
+  }
+  for (int j = 0; j < n_jobs; ++j) {
+    const nvfp4_quant_job &b = jobs[j];
+    int st = plan_quantize(b.x, b.rows, b.cols, b.ld_x, b.outs, b.n_outs, true, ws + j * kWsBytes, kWsBytes, &c[0]);
+    if (st == NVFP4_OK) st = launch_call(c[0], s);
+    if (st != NVFP4_OK) return st;
+  }
+  return finish(hipSuccess, s);
 }
 
 int nvfp4_quantize_noalloc(const void *x, int64_t rows, int64_t cols, int64_t ld_x, const nvfp4_quant_output *outs,

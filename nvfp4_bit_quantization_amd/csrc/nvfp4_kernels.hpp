@@ -120,6 +120,10 @@ hipError_t launch_mx_gemm(const MxGemmArgs &g, hipStream_t s);
 hipError_t launch_amax(const AmaxArgs &a, bool plain, bool rht_col, bool rht_row, int nparts, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int g1, bool rht1, bool sr1,
                            hipStream_t s, bool *supported);
+// two quantise calls, each with one RHT column output (sra, srb: stochastic
+// rounding), as one amax launch and one quantise launch
+hipError_t launch_quantize_batch2(const AmaxArgs &aa, const QuantArgs &qa, bool sra, const AmaxArgs &ab,
+                                  const QuantArgs &qb, bool srb, hipStream_t s);
 int quant_tiles(int64_t R, int64_t C);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 // GEMM workspace (stream-K path): kGemmMaxCUs flag words, an error word, then

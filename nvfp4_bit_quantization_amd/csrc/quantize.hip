@@ -8,18 +8,34 @@
 
 namespace nvfp4 {
 
+// amax pass: workgroup `part` of `nparts` takes tiles part, part + nparts, ...
+// and writes its partial maxima to slot `part`
 template <bool PLAIN, bool RC, bool RR>
-__global__ __launch_bounds__(kQThreads) void amax_kernel(AmaxArgs a) {
+__device__ __forceinline__ void amax_body(const AmaxArgs &a, uint32_t part, uint32_t nparts) {
   const int64_t ntiles = ((a.R + kQTileR - 1) / kQTileR) * ((a.C + kQTileC - 1) / kQTileC);
   float m_plain = 0.0f, m_rc = 0.0f, m_rr = 0.0f;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  for (int64_t t = part; t < ntiles; t += nparts) {
     const Lane L = lane_coords((uint32_t)t, a.R, a.C);
     if (!L.valid) continue;  // pairs of lanes are valid together (C % 16 == 0)
     uint4 raw[16];
     load_micro_tile(a.x, a.ld, L, raw);
     tile_maxes<PLAIN, RC, RR>(raw, L, a.mask_rows, a.mask_cols, m_plain, m_rc, m_rr);
   }
-  write_partials<PLAIN, RC, RR>(m_plain, m_rc, m_rr, a.partials, blockIdx.x);
+  write_partials<PLAIN, RC, RR>(m_plain, m_rc, m_rr, a.partials, part);
+}
+
+template <bool PLAIN, bool RC, bool RR>
+__global__ __launch_bounds__(kQThreads) void amax_kernel(AmaxArgs a) {
+  amax_body<PLAIN, RC, RR>(a, blockIdx.x, gridDim.x);
+}
+
+// The RHT-column amax passes of two tensors in one launch: the first na
+// workgroups serve a, the rest b.
+__global__ __launch_bounds__(kQThreads) void amax_batch2_kernel(AmaxArgs a, AmaxArgs b, uint32_t na) {
+  if (blockIdx.x < na)
+    amax_body<false, true, false>(a, blockIdx.x, na);
+  else
+    amax_body<false, true, false>(b, blockIdx.x - na, gridDim.x - na);
 }
 
 // Quantise pass: one micro-tile per lane, global scales from the partial
@@ -39,31 +55,61 @@ constexpr int quant_waves_per_simd() {
 // us; 16384 x 5120 row + column with the RHT 87.7 -> 84.7 us), although the
 // stage's registers hold the RHT-column RTN pairs to four waves per SIMD.  On
 // small tensors the extra barrier costs more than it saves.
+// quantise pass for one tile of the tensor (in the order of quant_tiles)
 template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1, bool STAGE = false>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(
-    quant_waves_per_simd<G0, RHT0, SR0, G1, RHT1, SR1, STAGE>()))) void quantize_kernel(QuantArgs a) {
+__device__ __forceinline__ void quantize_body(const QuantArgs &a, uint32_t tile) {
   constexpr int NOUT = (G1 == G_NONE) ? 1 : 2;
   __shared__ float s_lut[2][128];
   __shared__ float s_S[2];
   // tiles in row-major order (see quant_tiles); 256 x 128 ones for a single column output
   constexpr bool TALL = G0 == G_COL && G1 == G_NONE;
-  const Lane L = TALL ? lane_coords_tall(blockIdx.x, a.R, a.C) : lane_coords(blockIdx.x, a.R, a.C);
+  const Lane L = TALL ? lane_coords_tall(tile, a.R, a.C) : lane_coords(tile, a.R, a.C);
   float pm[2][4];
   load_partials<NOUT>(a, (uint32_t)a.nparts, pm);
   uint4 raw[16];
   load_micro_tile_any(a.x, a.ld, L, raw);
-  quant_setup<NOUT>(a, pm, s_S, s_lut);
+  quant_setup<NOUT>(a, pm, s_S, s_lut, tile == 0);
   if constexpr (STAGE) {
     __shared__ RowStage st;
     if (L.valid) quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut, &st);
     __syncthreads();  // every lane's row codes and scales are in the stage
     const int64_t ntc = (a.C + kQTileC - 1) / kQTileC;
-    row_stage_flush(&st, a.o[0], (int64_t)(blockIdx.x / ntc) * kQTileR, (int64_t)(blockIdx.x % ntc) * kQTileC, a.R,
-                    a.C);
+    row_stage_flush(&st, a.o[0], (int64_t)(tile / ntc) * kQTileR, (int64_t)(tile % ntc) * kQTileC, a.R, a.C);
   } else {
     if (!L.valid) return;
     quant_tile<G0, RHT0, SR0, G1, RHT1, SR1>(raw, L, a, s_S, s_lut);
   }
+}
+
+template <int G0, bool RHT0, bool SR0, int G1, bool RHT1, bool SR1, bool STAGE = false>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(
+    quant_waves_per_simd<G0, RHT0, SR0, G1, RHT1, SR1, STAGE>()))) void quantize_kernel(QuantArgs a) {
+  quantize_body<G0, RHT0, SR0, G1, RHT1, SR1, STAGE>(a, blockIdx.x);
+}
+
+// The quantise passes of two tensors, each with one RHT column output (the
+// Wgrad operands), in one launch.  Workgroups alternate between the two
+// (the first 2 min(ta, tb) block indices), the larger one's remaining tiles
+// come last, so every CU runs both at once: the stochastic-rounding pass is
+// bound by vector-ALU issue, the other by memory traffic, and they overlap.
+template <bool SRA, bool SRB>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(
+    quant_waves_per_simd<G_COL, true, SRA || SRB, G_NONE, false, false, false>()))) void quantize_batch2_kernel(
+    QuantArgs a, QuantArgs b, uint32_t ta, uint32_t tb) {
+  const uint32_t i = blockIdx.x, m = ta < tb ? ta : tb;
+  bool second;
+  uint32_t t;
+  if (i < 2 * m) {
+    second = (i & 1u) != 0;
+    t = i >> 1;
+  } else {
+    second = tb > ta;
+    t = i - m;
+  }
+  if (!second)
+    quantize_body<G_COL, true, SRA, G_NONE, false, false>(a, t);
+  else
+    quantize_body<G_COL, true, SRB, G_NONE, false, false>(b, t);
 }
 
 // 2D and 2D_T outputs, both rounded to nearest, from the same maximum (so
@@ -79,7 +125,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_tile_pair_kernel(QuantArgs
   load_partials<2>(a, (uint32_t)a.nparts, pm);
   uint4 raw[16];
   load_micro_tile_any(a.x, a.ld, L, raw);
-  quant_setup<2>(a, pm, s_S, s_lut);
+  quant_setup<2>(a, pm, s_S, s_lut, blockIdx.x == 0);
   if constexpr (STAGE) {
     __shared__ RowStage st;
     if (L.valid) tile_pair_rtn(raw, L, a.o[0], a.o[1], s_S[0], s_lut[0], a.R, a.C, &st);
@@ -228,6 +274,28 @@ hipError_t launch_quantize(const QuantArgs &a, int g0, bool rht0, bool sr0, int 
   }
   *supported = false;
   return hipErrorInvalidValue;
+}
+
+// The Wgrad operand pair: one amax launch (a's nparts workgroups, then b's)
+// and one quantise launch (quantize_batch2_kernel).
+hipError_t launch_quantize_batch2(const AmaxArgs &aa, const QuantArgs &qa, bool sra, const AmaxArgs &ab,
+                                  const QuantArgs &qb, bool srb, hipStream_t s) {
+  hipLaunchKernelGGL(amax_batch2_kernel, dim3((uint32_t)(qa.nparts + qb.nparts)), dim3(kQThreads), 0, s, aa, ab,
+                     (uint32_t)qa.nparts);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t ta = (uint32_t)(((qa.R + kQTallR - 1) / kQTallR) * ((qa.C + kQTallC - 1) / kQTallC));
+  const uint32_t tb = (uint32_t)(((qb.R + kQTallR - 1) / kQTallR) * ((qb.C + kQTallC - 1) / kQTallC));
+  const dim3 grid(ta + tb), block(kQThreads);
+  if (sra && srb)
+    hipLaunchKernelGGL((quantize_batch2_kernel<true, true>), grid, block, 0, s, qa, qb, ta, tb);
+  else if (sra)
+    hipLaunchKernelGGL((quantize_batch2_kernel<true, false>), grid, block, 0, s, qa, qb, ta, tb);
+  else if (srb)
+    hipLaunchKernelGGL((quantize_batch2_kernel<false, true>), grid, block, 0, s, qa, qb, ta, tb);
+  else
+    hipLaunchKernelGGL((quantize_batch2_kernel<false, false>), grid, block, 0, s, qa, qb, ta, tb);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s) {

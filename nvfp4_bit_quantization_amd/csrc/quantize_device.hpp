@@ -581,11 +581,12 @@ __device__ __forceinline__ void load_partials(const QuantArgs &a, uint32_t npart
 // the table r(c) = S / E4M3(c) of element factors (0 for the zero scale).
 // Threads 0-127 build output 0's table, threads 128-255 output 1's; each
 // thread derives its output's S itself from the wave maxima, so two barriers
-// serve both outputs.
+// serve both outputs.  The workgroup with `writer` set (the one that holds
+// the tensor's first tile) also stores S and amax.
 static_assert(kQThreads == 256, "one half of the workgroup per output table");
 template <int NOUT>
 __device__ __forceinline__ void quant_setup(const QuantArgs &a, const float pm[2][4], float s_S[2],
-                                            float s_lut[2][128]) {
+                                            float s_lut[2][128], bool writer) {
   __shared__ float s_red[2][kQThreads / 64];
   const uint32_t w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -602,7 +603,7 @@ __device__ __forceinline__ void quant_setup(const QuantArgs &a, const float pm[2
   if (amax == 0.0f || !__builtin_isfinite(S)) S = 1.0f;
   if (threadIdx.x == 128u * o) {
     s_S[o] = S;
-    if (blockIdx.x == 0) {
+    if (writer) {
       *a.o[o].S_out = S;
       *a.o[o].amax_out = amax;
     }

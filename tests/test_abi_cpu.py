@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_workspace_bytes",
+    for n in ("nvfp4_quantize", "nvfp4_quantize_batch", "nvfp4_quantize_noalloc", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_workspace_bytes",
               "nvfp4_rht_sign_mask",
               "nvfp4_status_string", "nvfp4_codec_selftest", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_gemm"):
         assert n in names
@@ -117,6 +117,38 @@ def test_quantize_noalloc_argument_validation(L):
     arr = (nv.nvfp4_quant_output * 1)(row)
     assert L.nvfp4_quantize_noalloc(None, 64, 32, 32, arr, 1, None) == -1
     assert L.nvfp4_quantize_noalloc(ctypes.c_void_p(FAKE), 64, 32, 32, None, 1, None) == -1
+
+
+def _job(outs, x=FAKE, rows=64, cols=32, ld=32):
+    arr = (nv.nvfp4_quant_output * max(1, len(outs)))(*outs)
+    return nv.nvfp4_quant_job(x, rows, cols, ld, ctypes.cast(arr, ctypes.POINTER(nv.nvfp4_quant_output)),
+                              len(outs)), arr
+
+
+def test_quantize_batch_argument_validation(L):
+    """The batch entry point rejects a bad batch, or any bad job in it, with
+    that job's nvfp4_quantize status, before anything is enqueued."""
+    row = _out(nv.ROW_1D, 64, 32, nv.SCALE_1D16)
+    colr = _out(nv.COL_1D, 32, 64, nv.SCALE_1D16, rht=1)
+    wsb = L.nvfp4_workspace_bytes()
+
+    def batch(specs, n=None, ws=FAKE, nbytes=None):
+        made = [_job(*s) if isinstance(s, tuple) else _job(s) for s in specs]
+        arr = (nv.nvfp4_quant_job * max(1, len(made)))(*[m[0] for m in made])
+        n = len(made) if n is None else n
+        nbytes = n * wsb if nbytes is None else nbytes
+        return L.nvfp4_quantize_batch(arr, n, ctypes.c_void_p(ws), nbytes, None)
+
+    assert L.nvfp4_quantize_batch(None, 1, ctypes.c_void_p(FAKE), wsb, None) == -1
+    assert batch([[row]], n=0) == -5
+    assert batch([[row]], ws=0) == -6
+    assert batch([[colr], [colr]], nbytes=2 * wsb - 1) == -6          # one slice per job
+    assert batch([[row]], ws=FAKE + 8) == -4
+    assert batch([([row], 0)]) == -1                                  # NULL x in the only job
+    assert batch([[colr], ([colr], FAKE, 24)]) == -2                  # the second job's shape
+    assert batch([[colr], ([colr], FAKE, 64, 32, 16)]) == -3          # the second job's ld
+    assert batch([[colr], [row, row]]) == -5                          # unsupported pair in a job
+    assert batch([[colr], []]) == -5                                  # a job without outputs
 
 
 def test_dequantize_and_gemm_validation(L):

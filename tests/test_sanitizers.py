@@ -134,6 +134,7 @@ namespace nvfp4 {
 static int launched = 0;
 hipError_t launch_amax(const AmaxArgs &, bool, bool, bool, int, hipStream_t) { ++launched; return hipErrorInvalidValue; }
 hipError_t launch_quantize(const QuantArgs &, int, bool, bool, int, bool, bool, hipStream_t, bool *s) { ++launched; *s = true; return hipErrorInvalidValue; }
+hipError_t launch_quantize_batch2(const AmaxArgs &, const QuantArgs &, bool, const AmaxArgs &, const QuantArgs &, bool, hipStream_t) { ++launched; return hipErrorInvalidValue; }
 int quant_tiles(int64_t R, int64_t C) { return (int)(((R + 127) / 128) * ((C + 255) / 256)); }
 hipError_t launch_dequantize(const DequantArgs &, hipStream_t) { ++launched; return hipErrorInvalidValue; }
 size_t gemm_workspace_bytes(int cus) { return kGemmWsSlots + (size_t)cus * kGemmSlotBytes; }
@@ -173,6 +174,21 @@ int main() {
   nvfp4_quant_output rr[2] = {row, row};
   CHECK(nvfp4_quantize(FAKE, 64, 32, 32, rr, 2, FAKE, wsb, nullptr) == NVFP4_E_UNSUPPORTED);
   CHECK(nvfp4_quantize(FAKE, (int64_t)1 << 20, (int64_t)1 << 15, (int64_t)1 << 15, &row, 1, FAKE, wsb, nullptr) == NVFP4_E_SHAPE);
+  nvfp4_quant_output colr = O(NVFP4_COL_1D, 32, 64, NVFP4_SCALE_1D16, 0, 1);
+  nvfp4_quant_job jobs[2];
+  memset(jobs, 0, sizeof jobs);
+  jobs[0].x = FAKE; jobs[0].rows = 64; jobs[0].cols = 32; jobs[0].ld_x = 32; jobs[0].outs = &colr; jobs[0].n_outs = 1;
+  jobs[1] = jobs[0];
+  CHECK(nvfp4_quantize_batch(nullptr, 1, FAKE, wsb, nullptr) == NVFP4_E_NULL);
+  CHECK(nvfp4_quantize_batch(jobs, 0, FAKE, wsb, nullptr) == NVFP4_E_UNSUPPORTED);
+  CHECK(nvfp4_quantize_batch(jobs, 2, FAKE, 2 * wsb - 1, nullptr) == NVFP4_E_WORKSPACE);
+  CHECK(nvfp4_quantize_batch(jobs, 2, (char *)FAKE + 8, 2 * wsb, nullptr) == NVFP4_E_ALIGN);
+  jobs[1].rows = 24;
+  CHECK(nvfp4_quantize_batch(jobs, 2, FAKE, 2 * wsb, nullptr) == NVFP4_E_SHAPE);
+  jobs[1].rows = 64; jobs[1].n_outs = 3;
+  CHECK(nvfp4_quantize_batch(jobs, 2, FAKE, 2 * wsb, nullptr) == NVFP4_E_UNSUPPORTED);
+  jobs[1].n_outs = 1; jobs[1].outs = nullptr;
+  CHECK(nvfp4_quantize_batch(jobs, 2, FAKE, 2 * wsb, nullptr) == NVFP4_E_NULL);
   CHECK(nvfp4_quantize_noalloc(nullptr, 64, 32, 32, &row, 1, nullptr) == NVFP4_E_NULL);
   CHECK(nvfp4_quantize_noalloc(FAKE, 64, 32, 16, &row, 1, nullptr) == NVFP4_E_LD);
   CHECK(nvfp4_quantize_noalloc(FAKE, 64, 32, 32, rr, 2, nullptr) == NVFP4_E_UNSUPPORTED);
