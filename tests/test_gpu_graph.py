@@ -5,7 +5,8 @@ replayed.  Each replay, with eager work and synchronisations in between, must
 reproduce the eager results bit for bit (stochastic rounding is keyed by the
 seed and block index, so it is deterministic too).  The step is the Wgrad path
 of the NVFP4 pretraining news page (zubnet.ai), paragraph 2, at a small shape,
-plus a row/column quantisation and a dequantisation."""
+plus a row/column quantisation and a dequantisation; the Wgrad operands are
+quantised by two calls, or by one batch call (the bench's form)."""
 import numpy as np
 import pytest
 
@@ -27,12 +28,14 @@ def nv():
     return nv
 
 
-def test_step_replays_from_a_graph(nv):
+@pytest.mark.parametrize("batch", [False, True])
+def test_step_replays_from_a_graph(nv, batch):
     T, H1, H2 = 2048, 768, 512
     dy = dev_bf16(syn.laplace(T, H1, seed=51, scale=1e-3))
     x = dev_bf16(syn.normal(T, H2, seed=52))
     a = dev_bf16(syn.activation(T, H2, seed=53))
     ws_dy, ws_x, ws_a = nv.new_workspace(), nv.new_workspace(), nv.new_workspace()
+    ws_b = nv.new_workspace(jobs=2)
     s_dy = [nv.QuantSpec.of("col", "sr", True, 1234, 1234)]
     s_x = [nv.QuantSpec.of("col", "rtn", True, 0, 1234)]
     s_a = [nv.QuantSpec.of("row"), nv.QuantSpec.of("col")]
@@ -43,15 +46,18 @@ def test_step_replays_from_a_graph(nv):
     y = torch.empty((T, H2), dtype=torch.float32, device="cuda")
 
     def step():
-        nv.nvfp4_quantize(dy, s_dy, q_dy, ws_dy)
-        nv.nvfp4_quantize(x, s_x, q_x, ws_x)
+        if batch:
+            nv.nvfp4_quantize_batch([(dy, s_dy, q_dy), (x, s_x, q_x)], ws_b)
+        else:
+            nv.nvfp4_quantize(dy, s_dy, q_dy, ws_dy)
+            nv.nvfp4_quantize(x, s_x, q_x, ws_x)
         nv.nvfp4_gemm(q_dy[0], q_x[0], c)
         nv.nvfp4_quantize(a, s_a, q_a, ws_a)
         nv.nvfp4_dequantize(q_a[0], y)
 
     outs = [q_dy[0].codes, q_dy[0].scales, q_dy[0].global_scale, q_x[0].codes, q_x[0].scales, c,
             q_a[0].codes, q_a[1].codes, q_a[1].scales, y]
-    say("graph: eager step")
+    say("graph: eager step, batch", batch)
     step()
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs]
