@@ -167,9 +167,8 @@ typedef struct {
  * Two jobs that each have a single NVFP4_COL_1D output with the RHT and
  * flags 0 (the weight-gradient operand pair; either rounding for each) run as
  * one amax launch and one quantise launch whose workgroups alternate between
- * the two inputs, so that the arithmetic of one overlaps the memory traffic
- * of the other.  Any other batch enqueues its jobs one after another, as
- * nvfp4_quantize would.
+ * the two inputs (two kernel launches instead of four).  Any other batch
+ * enqueues its jobs one after another, as nvfp4_quantize would.
  * Returns NVFP4_OK or a negative status: NVFP4_E_NULL for jobs == NULL,
  * NVFP4_E_UNSUPPORTED for n_jobs < 1, NVFP4_E_WORKSPACE or NVFP4_E_ALIGN for
  * the workspace, else the first failing job's status.  Every job is checked
