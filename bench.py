@@ -506,11 +506,12 @@ def cpu_baseline(workload: str, syn):
                            "quantise %.2f s, GEMM estimated as the BLAS time x its threads"
                            % (qthreads, t1 - t0, blas_threads, t2 - t1, tq1))
     if workload in ("act_8192x5120", "weight_5120x20480", "tiny_256"):
+        # the whole workload (the same tensor the GPU quantises)
         if workload == "act_8192x5120":
-            bits, specs = syn.act_8192x5120(2048, 5120), ["row", "col"]
-            nbytes = qbytes(2048, 5120, 2)
+            bits, specs = syn.act_8192x5120(), ["row", "col"]
+            nbytes = qbytes(8192, 5120, 2)
         elif workload == "weight_5120x20480":
-            bits, specs = syn.weight_5120x20480(1280, 20480), ["2d", "2d_t"]
+            bits, specs = syn.weight_5120x20480(), ["2d", "2d_t"]
             nbytes = 2 * bits.size + 2 * (bits.size // 2 + bits.size // 256)
         else:
             bits, specs = syn.tiny_256(), ["row"]
@@ -522,7 +523,7 @@ def cpu_baseline(workload: str, syn):
         dt1 = one_thread(lambda: [oracle.quantize(bits, s) for s in specs])
         return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=qthreads, kind="oracle",
                     value_1thread=nbytes / dt1 / 1e9,
-                    sample="%s quantise of a %dx%d slice (C oracle, %d threads, %.2f s; 1 thread %.2f s)" % (
+                    sample="%s quantise of the whole %dx%d tensor (C oracle, %d threads, %.2f s; 1 thread %.2f s)" % (
                         "+".join(specs), bits.shape[0], bits.shape[1], qthreads, dt, dt1))
     # linear step: one Wgrad GEMM + its two quantisations on a 1/8 token slice
     tokens, hidden, ffn = 2048, 5120, 2560
